@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs for the decode-step workloads.
+
+This module only draws random numbers and shapes them (normalisation, fixed per-row/column
+scale factors).  It holds none of the method's arithmetic: no state update, no quantizer, no
+allocation.  Both the oracle-side tests and the product-side benchmark draw their inputs here.
+
+Shapes follow the deployment the "STEPQuant" digest describes (Background: Qwen GDN heads with
+d_k = d_v = 128 at tens of concurrent requests; Method 1: 2,304 GDN heads with 32 FP16 pivot
+heads, 81,920 KDA key rows with 512 FP16 pivot rows, nominal 4-bit widths {2,4,6,8} and
+nominal 6-bit widths {4,6,8}; Method 3: max/median RMS contrasts of about 10x over key rows and
+19x over value columns).  No dataset is involved: every tensor is drawn from NumPy PCG64 with a
+seed derived from 20261203 + the workload number.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+SEED_BASE = 20261203
+
+# stream ids: independent draws per purpose
+_PLAN, _WARM, _DECODE, _GEOM, _CALIB = 1, 2, 3, 4, 5
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic decode workload."""
+    wid: int
+    name: str
+    kind: str                  # "gdn" (unit = head, scalar gate) or "kda" (unit = key row)
+    B: int                     # concurrent requests
+    layers: int
+    H: int                     # heads per layer
+    d: int                     # d_k = d_v
+    steps: int                 # decode steps
+    warmup: int                # unquantized warm-up steps that build the initial state
+    choices: tuple             # allowed widths
+    nominal: int               # nominal average width (budget)
+    n_pivots: int              # FP16 pivot units (heads for GDN, rows for KDA)
+    alloc: str                 # "fixed", "mcdp" or "lagrangian"
+    du: str = "synthetic"      # "synthetic" (s_u 2^-2b) or "measured"
+    contrast: bool = False     # lognormal row/column geometry
+    split: bool = False        # refit and writeback on a side stream
+    fixed_bits: tuple = ()     # per-head widths for alloc == "fixed" (0 = FP16 pivot head)
+    calib_steps: int = 0       # calibration steps for omega (KDA); 0 = use the warm-up
+    horizon: int = 512         # H of the lifetime weight
+
+    @property
+    def tiles_per_layer(self) -> int:
+        return self.B * self.H
+
+
+def _pivots(frac_num, frac_den, units):
+    return int(round(units * frac_num / frac_den))
+
+
+WORKLOADS = {
+    1: Workload(1, "tiny-gdn", "gdn", B=2, layers=1, H=4, d=64, steps=32, warmup=16,
+                choices=(4, 6, 8), nominal=6, n_pivots=1, alloc="fixed",
+                fixed_bits=(4, 6, 8, 0)),
+    2: Workload(2, "gdn6-70x48", "gdn", B=70, layers=1, H=48, d=128, steps=256, warmup=16,
+                choices=(4, 6, 8), nominal=6, n_pivots=_pivots(32, 2304, 48), alloc="mcdp"),
+    3: Workload(3, "gdn4-128x48-contrast", "gdn", B=128, layers=1, H=48, d=128, steps=256,
+                warmup=16, choices=(2, 4, 6, 8), nominal=4, n_pivots=1, alloc="mcdp",
+                contrast=True),
+    4: Workload(4, "kda6-64x32", "kda", B=64, layers=1, H=32, d=128, steps=256, warmup=16,
+                choices=(4, 6, 8), nominal=6, n_pivots=_pivots(512, 81920, 32 * 128),
+                alloc="lagrangian", du="measured", calib_steps=64),
+    5: Workload(5, "gdn6-stress-256x12x48", "gdn", B=256, layers=12, H=48, d=128, steps=128,
+                warmup=16, choices=(4, 6, 8), nominal=6, n_pivots=_pivots(32, 2304, 576),
+                alloc="mcdp", split=True),
+}
+
+
+def _rng(wid: int, *stream) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_BASE + wid,
+                                                                       *stream])))
+
+
+def _normalize(x):
+    x = np.asarray(x, np.float64)
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def plan_tables(w: Workload):
+    """Per-unit gate log-means l_u ~ U(-0.2, -0.001) and distortion scales s_u ~ LogNormal(0, 1)
+    for the synthetic distortion table d_u(b) = s_u 2^(-2b).  Units: layers*H heads (GDN) or
+    layers*H*d key rows (KDA)."""
+    g = _rng(w.wid, _PLAN)
+    units = w.layers * w.H * (w.d if w.kind == "kda" else 1)
+    l_u = g.uniform(-0.2, -0.001, size=units)
+    s_u = g.lognormal(0.0, 1.0, size=units)
+    return l_u, s_u
+
+
+def synthetic_distortion(s_u, choices):
+    """d_u(b) = s_u 2^(-2b): the rate-distortion shape of a uniform quantizer."""
+    b = np.asarray(choices, np.float64)
+    return np.asarray(s_u, np.float64)[:, None] * np.exp2(-2.0 * b)[None, :]
+
+
+def geometry(w: Workload, layer: int):
+    """Fixed per-(request, head) key-row and value-column factors rho, gamma ~ exp(N(0, 1)),
+    used by the high-contrast workload; ones otherwise."""
+    if not w.contrast:
+        return None, None
+    g = _rng(w.wid, _GEOM, layer)
+    rho = np.exp(g.standard_normal((w.B, w.H, w.d)))
+    gam = np.exp(g.standard_normal((w.B, w.H, w.d)))
+    return rho, gam
+
+
+def step_inputs(w: Workload, layer: int, step: int, phase: str = "decode"):
+    """Inputs of one step of one layer: q, k, v [B, H, d] float32 (q, k L2-normalised),
+    alpha [B, H] (GDN, exp(-softplus(N(-4, 0.5)))) or [B, H, d] (KDA, U(0.8, 1)),
+    beta [B, H] = sigmoid(N(0, 1)).  phase selects an independent stream: "warmup",
+    "decode" or "calib"."""
+    sid = {"warmup": _WARM, "decode": _DECODE, "calib": _CALIB}[phase]
+    g = _rng(w.wid, sid, layer, step)
+    shp = (w.B, w.H, w.d)
+    q = g.standard_normal(shp)
+    k = g.standard_normal(shp)
+    v = g.standard_normal(shp)
+    beta = 1.0 / (1.0 + np.exp(-g.standard_normal((w.B, w.H))))
+    if w.kind == "gdn":
+        x = g.normal(-4.0, 0.5, size=(w.B, w.H))
+        alpha = np.exp(-np.logaddexp(0.0, x))
+    else:
+        alpha = g.uniform(0.8, 1.0, size=shp)
+    rho, gam = geometry(w, layer)
+    if rho is not None:
+        k = rho * k
+        v = gam * v
+    q, k = _normalize(q), _normalize(k)
+    f = lambda x: np.ascontiguousarray(x, dtype=np.float32)
+    return dict(q=f(q), k=f(k), v=f(v), alpha=f(alpha), beta=f(beta))
+
+
+def alpha_rows(w: Workload, alpha):
+    """Per-row gate a_i of every tile: GDN broadcasts the scalar gate over the d_k rows."""
+    alpha = np.asarray(alpha, np.float32)
+    if w.kind == "gdn":
+        return np.ascontiguousarray(np.broadcast_to(alpha[..., None], alpha.shape + (w.d,)))
+    return alpha

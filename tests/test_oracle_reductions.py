@@ -1,0 +1,55 @@
+"""Pins for the oracle's fixed-order sums: values whose result depends on the order (so a wrong
+tree shape or a missing fused multiply-add fails), and error bounds against exact sums."""
+from fractions import Fraction
+
+import numpy as np
+
+
+def test_tree_order_pin(orc):
+    # pairwise: (1e8 + 1) + (-1e8 + 1) = 1e8 + (-1e8) = 0 in binary32; left to right gives 1
+    x = np.array([1e8, 1.0, -1e8, 1.0], np.float32)
+    assert orc.tree_sum(x) == np.float32(0.0)
+    # eight terms: ((a+b)+(c+d)) + ((e+f)+(g+h))
+    x = np.array([1.0, 2 ** 24, -(2 ** 24), 1.0, 3.0, 0.0, 0.0, 0.0], np.float32)
+    a = np.float32(np.float32(1.0) + np.float32(2 ** 24))
+    b = np.float32(np.float32(-(2 ** 24)) + np.float32(1.0))
+    assert orc.tree_sum(x) == np.float32(np.float32(a + b) + np.float32(3.0))
+
+
+def _fma32(a, b, c):
+    return np.float32(Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c)))
+
+
+def test_dot_order_pin(orc):
+    # group of four: s = x0*y0; s = fma(x1,y1,s); s = fma(x2,y2,s); s = fma(x3,y3,s)
+    g = np.random.default_rng(7)
+    for _ in range(200):
+        x = g.standard_normal(8).astype(np.float32)
+        y = g.standard_normal(8).astype(np.float32)
+        quads = []
+        for m in range(2):
+            s = np.float32(x[4 * m] * y[4 * m])
+            for t in range(1, 4):
+                s = _fma32(x[4 * m + t], y[4 * m + t], s)
+            quads.append(s)
+        assert orc.dot(x, y) == np.float32(quads[0] + quads[1])
+    # a case where the fused and the separately rounded evaluation differ
+    x = np.array([1.0, 1 + 2 ** -12, 0, 0], np.float32)
+    y = np.array([-1.0, 1 + 2 ** -12, 0, 0], np.float32)
+    fused = np.float32(Fraction(float(x[1])) ** 2 - 1)
+    assert orc.dot(x, y) == fused
+    assert fused != np.float32(np.float32(x[1] * y[1]) - np.float32(1.0))
+
+
+def test_sums_within_error_bound(orc):
+    g = np.random.default_rng(3)
+    u = 2.0 ** -24
+    for n in (4, 8, 64, 128):
+        for _ in range(50):
+            x = g.standard_normal(n).astype(np.float32)
+            y = g.standard_normal(n).astype(np.float32)
+            exact = float(sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x, y)))
+            bound = (np.log2(n) + 4) * u * float(np.sum(np.abs(x.astype(np.float64) * y)))
+            assert abs(float(orc.dot(x, y)) - exact) <= bound
+            ex = float(sum(Fraction(float(a)) for a in x))
+            assert abs(float(orc.tree_sum(x)) - ex) <= np.log2(n) * u * float(np.sum(np.abs(x)))
