@@ -1,0 +1,418 @@
+// stepq_api.cpp -- host side of libstepq.so: argument checks, packed layout, plan tables,
+// launches and stream ordering.  The ABI is declared (and each call documented) in stepq.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "stepq.h"
+#include "stepq_internal.h"
+
+using namespace stepq;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return STEPQ_OK;
+}
+
+#define HIP_TRY(expr)                                                                    \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return fail(STEPQ_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));         \
+  } while (0)
+
+// Pairwise tree sum in binary32, the same evaluation order as the kernels' reductions.
+float tree_sum(const float* x, int n) {
+  if (n == 1) return x[0];
+  return tree_sum(x, n / 2) + tree_sum(x + n / 2, n - n / 2);
+}
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok_ = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(dev) == hipSuccess) ok_ = true;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+struct stepq_plan {
+  int kind = 0, H = 0, D = 0, mode = 0, max_batch = 0, device = 0;
+  long long bpr = 0;
+  double bpv = 0.0;
+  std::vector<long long> head_off, head_bytes;
+  void* dtab = nullptr;     // all device tables in one allocation
+  unsigned* status = nullptr;
+  float* stash = nullptr;   // split-mode hand-over
+  DevPlan dp{};
+  hipStream_t side = nullptr;
+  hipEvent_t ev_read = nullptr, ev_write = nullptr;
+  bool write_pending = false;
+  long long spin_cycles = 0;
+};
+
+namespace {
+
+int check_plan(stepq_plan_t p) {
+  if (!p) return fail(STEPQ_ERR_INVALID_ARG, "plan is NULL");
+  return STEPQ_OK;
+}
+
+void destroy_plan(stepq_plan* p) {
+  if (!p) return;
+  if (p->side) (void)hipStreamSynchronize(p->side);
+  if (p->ev_read) (void)hipEventDestroy(p->ev_read);
+  if (p->ev_write) (void)hipEventDestroy(p->ev_write);
+  if (p->side) (void)hipStreamDestroy(p->side);
+  if (p->stash) (void)hipFree(p->stash);
+  if (p->dtab) (void)hipFree(p->dtab);
+  delete p;
+}
+
+// Orders `stream` after the plan's pending side-stream writeback (split mode).
+hipError_t wait_writeback(stepq_plan* p, hipStream_t stream) {
+  if (p->mode == STEPQ_MODE_SPLIT && p->write_pending) return hipStreamWaitEvent(stream, p->ev_write, 0);
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* stepq_last_error(void) { return g_err.c_str(); }
+
+int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
+  if (!d || !out) return fail(STEPQ_ERR_INVALID_ARG, "desc and out must be non-NULL");
+  *out = nullptr;
+  if (d->kind != STEPQ_KIND_GDN && d->kind != STEPQ_KIND_KDA)
+    return fail(STEPQ_ERR_INVALID_ARG, "kind must be STEPQ_KIND_GDN or STEPQ_KIND_KDA");
+  if (d->n_heads < 1) return fail(STEPQ_ERR_INVALID_ARG, "n_heads must be >= 1");
+  if (d->d_k != d->d_v) return fail(STEPQ_ERR_UNSUPPORTED, "this build supports d_k == d_v only");
+  if (d->d_k != 64 && d->d_k != 128)
+    return fail(STEPQ_ERR_UNSUPPORTED, "d_k must be 64 or 128 (got %d)", d->d_k);
+  if (!d->bits || !d->pivot || !d->omega)
+    return fail(STEPQ_ERR_INVALID_ARG, "bits, pivot and omega must be non-NULL");
+  if (d->mode != STEPQ_MODE_FUSED && d->mode != STEPQ_MODE_SPLIT)
+    return fail(STEPQ_ERR_INVALID_ARG, "mode must be STEPQ_MODE_FUSED or STEPQ_MODE_SPLIT");
+  if (d->mode == STEPQ_MODE_SPLIT && d->max_batch < 1)
+    return fail(STEPQ_ERR_INVALID_ARG, "split mode needs max_batch >= 1");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || d->device < 0 || d->device >= ndev)
+    return fail(STEPQ_ERR_INVALID_ARG, "device %d not available (%d devices)", d->device, ndev);
+
+  const int H = d->n_heads, D = d->d_k, G = D / 64;
+  const long long nrow = (long long)H * D;
+  for (long long i = 0; i < nrow; i++) {
+    if (d->pivot[i] > 1) return fail(STEPQ_ERR_INVALID_ARG, "pivot[%lld] must be 0 or 1", i);
+    const int b = d->bits[i];
+    if (!d->pivot[i] && b != 2 && b != 4 && b != 6 && b != 8)
+      return fail(STEPQ_ERR_INVALID_ARG, "bits[%lld] = %d not in {2,4,6,8}", i, b);
+    if (!std::isfinite(d->omega[i]) || d->omega[i] < 0.0f)
+      return fail(STEPQ_ERR_INVALID_ARG, "omega[%lld] must be finite and >= 0", i);
+  }
+
+  // per-head layout (segment: code block, pivot rows, row factors, column factors)
+  std::vector<int> head_type(H), off_piv(H), off_r(H), off_c(H), words(H);
+  std::vector<long long> head_off(H), head_bytes(H);
+  std::vector<float> den(nrow), qmax(nrow), iq(nrow), omega(d->omega, d->omega + nrow);
+  std::vector<int> bits(nrow), rowpos(nrow), pividx(nrow);
+  long long off = 0;
+  for (int h = 0; h < H; h++) {
+    const int8_t* hb = d->bits + (long long)h * D;
+    const uint8_t* hp = d->pivot + (long long)h * D;
+    int npiv = 0, b0 = -1;
+    bool uniform = true;
+    long long lane_bits = 0;
+    for (int i = 0; i < D; i++) {
+      const long long r = (long long)h * D + i;
+      if (hp[i]) {
+        pividx[r] = npiv++;
+        rowpos[r] = -1;
+        bits[r] = 0;
+        qmax[r] = 0.0f;
+        iq[r] = 0.0f;
+      } else {
+        pividx[r] = -1;
+        rowpos[r] = (int)lane_bits;
+        bits[r] = hb[i];
+        lane_bits += (long long)G * hb[i];
+        qmax[r] = (float)((1 << (hb[i] - 1)) - 1);
+        iq[r] = 1.0f / qmax[r];
+        if (b0 < 0) b0 = hb[i];
+        else if (hb[i] != b0) uniform = false;
+      }
+    }
+    const bool allpiv = npiv == D;
+    if (d->kind == STEPQ_KIND_GDN) {
+      if (npiv != 0 && !allpiv)
+        return fail(STEPQ_ERR_INVALID_ARG, "GDN head %d: pivot must cover all or none of its rows", h);
+      if (!uniform)
+        return fail(STEPQ_ERR_INVALID_ARG, "GDN head %d: all rows must share one width", h);
+      head_type[h] = allpiv ? kHeadPivot : b0;
+    } else {
+      head_type[h] = kHeadMixed;
+    }
+    words[h] = (int)((lane_bits + 31) / 32);
+    off_piv[h] = 256 * words[h];
+    off_r[h] = off_piv[h] + 2 * D * npiv;
+    off_c[h] = off_r[h] + (allpiv ? 0 : 2 * D);
+    const long long end = off_c[h] + (allpiv ? 0 : 2 * D);
+    head_bytes[h] = (end + 255) / 256 * 256;
+    head_off[h] = off;
+    off += head_bytes[h];
+    // den_i = 1 + omega_i / mean(omega): mean as a pairwise tree times 1/d
+    const float* ho = d->omega + (long long)h * D;
+    const float mean = tree_sum(ho, D) * (1.0f / (float)D);
+    for (int i = 0; i < D; i++) den[(long long)h * D + i] = mean > 0.0f ? 1.0f + ho[i] / mean : 1.0f;
+  }
+
+  auto* p = new (std::nothrow) stepq_plan();
+  if (!p) return fail(STEPQ_ERR_OOM, "host allocation failed");
+  p->kind = d->kind;
+  p->H = H;
+  p->D = D;
+  p->mode = d->mode;
+  p->max_batch = d->max_batch;
+  p->device = d->device;
+  p->bpr = off;
+  p->bpv = 8.0 * (double)off / ((double)H * D * D);
+  p->head_off = head_off;
+  p->head_bytes = head_bytes;
+
+  DeviceGuard dg(d->device);
+  if (!dg.ok_) {
+    destroy_plan(p);
+    return fail(STEPQ_ERR_HIP, "hipSetDevice(%d) failed", d->device);
+  }
+  // one device allocation for every table, each 256-byte aligned
+  struct Piece { const void* src; size_t bytes; size_t off; };
+  std::vector<Piece> pieces;
+  size_t total = 0;
+  auto add = [&](const void* src, size_t bytes) {
+    pieces.push_back({src, bytes, total});
+    total += (bytes + 255) / 256 * 256;
+    return pieces.size() - 1;
+  };
+  const size_t i_hoff = add(head_off.data(), H * sizeof(long long));
+  const size_t i_type = add(head_type.data(), H * sizeof(int));
+  const size_t i_opiv = add(off_piv.data(), H * sizeof(int));
+  const size_t i_or = add(off_r.data(), H * sizeof(int));
+  const size_t i_oc = add(off_c.data(), H * sizeof(int));
+  const size_t i_w = add(words.data(), H * sizeof(int));
+  const size_t i_den = add(den.data(), nrow * sizeof(float));
+  const size_t i_om = add(omega.data(), nrow * sizeof(float));
+  const size_t i_qm = add(qmax.data(), nrow * sizeof(float));
+  const size_t i_iq = add(iq.data(), nrow * sizeof(float));
+  const size_t i_bits = add(bits.data(), nrow * sizeof(int));
+  const size_t i_pos = add(rowpos.data(), nrow * sizeof(int));
+  const size_t i_pid = add(pividx.data(), nrow * sizeof(int));
+  const unsigned zero = 0;
+  const size_t i_st = add(&zero, sizeof(unsigned));
+  hipError_t e = hipMalloc(&p->dtab, total);
+  if (e != hipSuccess) {
+    destroy_plan(p);
+    return fail(STEPQ_ERR_OOM, "hipMalloc(%zu) for plan tables: %s", total, hipGetErrorString(e));
+  }
+  for (const Piece& pc : pieces) {
+    e = hipMemcpy((char*)p->dtab + pc.off, pc.src, pc.bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      destroy_plan(p);
+      return fail(STEPQ_ERR_HIP, "plan table upload: %s", hipGetErrorString(e));
+    }
+  }
+  auto at = [&](size_t i) { return (void*)((char*)p->dtab + pieces[i].off); };
+  DevPlan& dp = p->dp;
+  dp.H = H;
+  dp.D = D;
+  dp.bpr = p->bpr;
+  dp.head_off = (const long long*)at(i_hoff);
+  dp.head_type = (const int*)at(i_type);
+  dp.off_piv = (const int*)at(i_opiv);
+  dp.off_r = (const int*)at(i_or);
+  dp.off_c = (const int*)at(i_oc);
+  dp.words = (const int*)at(i_w);
+  dp.den = (const float*)at(i_den);
+  dp.omega = (const float*)at(i_om);
+  dp.qmax = (const float*)at(i_qm);
+  dp.iq = (const float*)at(i_iq);
+  dp.bits = (const int*)at(i_bits);
+  dp.rowpos = (const int*)at(i_pos);
+  dp.pividx = (const int*)at(i_pid);
+  dp.status = (unsigned*)at(i_st);
+  p->status = dp.status;
+
+  if (d->mode == STEPQ_MODE_SPLIT) {
+    const size_t n = (size_t)d->max_batch * H * 4 * D * sizeof(float);
+    e = hipMalloc((void**)&p->stash, n);
+    if (e != hipSuccess) {
+      destroy_plan(p);
+      return fail(STEPQ_ERR_OOM, "hipMalloc(%zu) for the split-mode hand-over: %s", n,
+                  hipGetErrorString(e));
+    }
+    if ((e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&p->ev_read, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&p->ev_write, hipEventDisableTiming)) != hipSuccess) {
+      destroy_plan(p);
+      return fail(STEPQ_ERR_HIP, "side stream / events: %s", hipGetErrorString(e));
+    }
+  }
+  *out = p;
+  return ok();
+}
+
+int stepq_plan_destroy(stepq_plan_t p) {
+  if (!p) return ok();
+  DeviceGuard dg(p->device);
+  destroy_plan(p);
+  return ok();
+}
+
+int stepq_pool_bytes(stepq_plan_t p, size_t* bytes_per_request, double* bits_per_value) {
+  if (int rc = check_plan(p)) return rc;
+  if (bytes_per_request) *bytes_per_request = (size_t)p->bpr;
+  if (bits_per_value) *bits_per_value = p->bpv;
+  return ok();
+}
+
+int stepq_head_segment(stepq_plan_t p, int head, size_t* offset, size_t* bytes) {
+  if (int rc = check_plan(p)) return rc;
+  if (head < 0 || head >= p->H) return fail(STEPQ_ERR_INVALID_ARG, "head %d out of range", head);
+  if (offset) *offset = (size_t)p->head_off[head];
+  if (bytes) *bytes = (size_t)p->head_bytes[head];
+  return ok();
+}
+
+static int check_pool(const void* pool, int B) {
+  if (B < 0) return fail(STEPQ_ERR_INVALID_ARG, "B must be >= 0");
+  if (B > 0 && !pool) return fail(STEPQ_ERR_INVALID_ARG, "pool is NULL");
+  if (((uintptr_t)pool & 255u) != 0) return fail(STEPQ_ERR_INVALID_ARG, "pool must be 256-byte aligned");
+  return STEPQ_OK;
+}
+
+int stepq_encode_state(stepq_plan_t p, const float* S, void* pool, int B, void* stream) {
+  if (int rc = check_plan(p)) return rc;
+  if (int rc = check_pool(pool, B)) return rc;
+  if (B > 0 && !S) return fail(STEPQ_ERR_INVALID_ARG, "S is NULL");
+  if (p->mode == STEPQ_MODE_SPLIT && B > p->max_batch)
+    return fail(STEPQ_ERR_INVALID_ARG, "B = %d exceeds max_batch %d", B, p->max_batch);
+  DeviceGuard dg(p->device);
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(wait_writeback(p, s));
+  StepArgs a{};
+  a.P = p->dp;
+  a.pool = (uint8_t*)pool;
+  a.B = B;
+  a.S_in = S;
+  a.stash = p->stash;
+  HIP_TRY(launch_step(p->kind, ENCODE, a, s));
+  return ok();
+}
+
+int stepq_decode_step(stepq_plan_t p, void* pool, int B, const float* q, const float* k,
+                      const float* v, const float* alpha, const float* beta, float* out,
+                      void* stream) {
+  if (int rc = check_plan(p)) return rc;
+  if (int rc = check_pool(pool, B)) return rc;
+  if (B > 0 && (!q || !k || !v || !alpha || !beta || !out))
+    return fail(STEPQ_ERR_INVALID_ARG, "q, k, v, alpha, beta and out must be non-NULL");
+  if (p->mode == STEPQ_MODE_SPLIT && B > p->max_batch)
+    return fail(STEPQ_ERR_INVALID_ARG, "B = %d exceeds max_batch %d", B, p->max_batch);
+  if (B == 0) return ok();
+  DeviceGuard dg(p->device);
+  hipStream_t s = (hipStream_t)stream;
+  StepArgs a{};
+  a.P = p->dp;
+  a.pool = (uint8_t*)pool;
+  a.B = B;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.out = out;
+  a.stash = p->stash;
+  if (p->mode == STEPQ_MODE_FUSED) {
+    HIP_TRY(launch_step(p->kind, FUSED, a, s));
+    return ok();
+  }
+  // split: readout on the caller's stream; refit + pack on the side stream once it is done
+  HIP_TRY(wait_writeback(p, s));
+  HIP_TRY(launch_step(p->kind, READ, a, s));
+  HIP_TRY(hipEventRecord(p->ev_read, s));
+  HIP_TRY(hipStreamWaitEvent(p->side, p->ev_read, 0));
+  if (p->spin_cycles > 0) HIP_TRY(launch_spin(p->spin_cycles, p->side));
+  HIP_TRY(launch_step(p->kind, WRITE, a, p->side));
+  HIP_TRY(hipEventRecord(p->ev_write, p->side));
+  p->write_pending = true;
+  return ok();
+}
+
+int stepq_unpack_debug(stepq_plan_t p, const void* pool, int B, float* S_hat, uint16_t* r,
+                       uint16_t* c, int8_t* z, void* stream) {
+  if (int rc = check_plan(p)) return rc;
+  if (int rc = check_pool(pool, B)) return rc;
+  DeviceGuard dg(p->device);
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(wait_writeback(p, s));
+  HIP_TRY(launch_unpack(p->dp, (const uint8_t*)pool, B, S_hat, r, c, z, s));
+  return ok();
+}
+
+int stepq_sync(stepq_plan_t p) {
+  if (int rc = check_plan(p)) return rc;
+  DeviceGuard dg(p->device);
+  if (p->side) HIP_TRY(hipStreamSynchronize(p->side));
+  return ok();
+}
+
+int stepq_get_status(stepq_plan_t p, uint32_t* flags, int reset) {
+  if (int rc = check_plan(p)) return rc;
+  if (!flags) return fail(STEPQ_ERR_INVALID_ARG, "flags is NULL");
+  DeviceGuard dg(p->device);
+  HIP_TRY(hipDeviceSynchronize());
+  unsigned v = 0;
+  HIP_TRY(hipMemcpy(&v, p->status, sizeof v, hipMemcpyDeviceToHost));
+  *flags = v;
+  if (reset) {
+    const unsigned zero = 0;
+    HIP_TRY(hipMemcpy(p->status, &zero, sizeof zero, hipMemcpyHostToDevice));
+  }
+  return ok();
+}
+
+// Test hook: a bounded spin of `cycles` clocks on the side stream before each split-mode
+// writeback, to show that the next step's readout waits for it.
+int stepq_debug_side_delay(stepq_plan_t p, long long cycles) {
+  if (int rc = check_plan(p)) return rc;
+  if (cycles < 0 || cycles > 2000000000LL)
+    return fail(STEPQ_ERR_INVALID_ARG, "cycles must be in [0, 2e9]");
+  p->spin_cycles = cycles;
+  return ok();
+}
+
+}  // extern "C"

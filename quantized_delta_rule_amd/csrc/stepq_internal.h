@@ -1,0 +1,60 @@
+// stepq_internal.h -- shared between the host API (stepq_api.cpp) and the kernels
+// (stepq_kernels.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace stepq {
+
+// Head types of the per-head dispatch: 2/4/6/8 = head quantized at that width (GDN),
+// 0 = FP16 pivot head (GDN), -1 = rows of mixed widths and pivots (KDA).
+constexpr int kHeadPivot = 0;
+constexpr int kHeadMixed = -1;
+
+// Kernel modes.  FUSED: the whole step.  READ: decode, update, readout, hand-over of the
+// per-row/per-column update factors.  WRITE: decode, update from the hand-over, refit, pack.
+// ENCODE: refit and pack an fp32 state given in memory.
+enum Mode { FUSED = 0, READ = 1, WRITE = 2, ENCODE = 3 };
+
+// Device-resident plan tables (all arrays in device memory; per-row arrays are [H * d]).
+struct DevPlan {
+  int H, D;                  // heads, d_k = d_v
+  long long bpr;             // bytes per request
+  const long long* head_off; // [H] segment byte offset inside one request
+  const int* head_type;      // [H]
+  const int* off_piv;        // [H] pivot block offset inside the segment
+  const int* off_r;          // [H] row-factor block offset
+  const int* off_c;          // [H] column-factor block offset
+  const int* words;          // [H] words per lane of the code block
+  const float* den;          // [H*d] 1 + omega_i / mean(omega)
+  const float* omega;        // [H*d]
+  const float* qmax;         // [H*d] 2^(b-1)-1, 0 on pivot rows
+  const float* iq;           // [H*d] 1/qmax, 0 on pivot rows
+  const int* bits;           // [H*d] width (0 on pivot rows)
+  const int* rowpos;         // [H*d] stream bit offset of the row's first code (-1 on pivots)
+  const int* pividx;         // [H*d] row index inside the pivot block (-1 otherwise)
+  unsigned* status;          // accumulated STEPQ_FLAG_* bits
+};
+
+struct StepArgs {
+  DevPlan P;
+  uint8_t* pool;
+  int B;
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* alpha;
+  const float* beta;
+  float* out;
+  float* stash;      // split-mode hand-over, [B*H][4*D]
+  const float* S_in; // ENCODE input [B*H][D][D]
+};
+
+// Launchers (stepq_kernels.hip).  kind: 0 = GDN, 1 = KDA.
+hipError_t launch_step(int kind, Mode mode, const StepArgs& a, hipStream_t s);
+hipError_t launch_unpack(const DevPlan& P, const uint8_t* pool, int B, float* S, uint16_t* r,
+                         uint16_t* c, int8_t* z, hipStream_t s);
+hipError_t launch_spin(long long cycles, hipStream_t s);
+
+}  // namespace stepq

@@ -1,0 +1,253 @@
+"""Helpers of the GPU parity tests: the oracle builds every plan, initial state and expected
+value; the GPU library runs the same seeded inputs through its C ABI; results are compared per
+step with the acceptance rule of the decode path:
+
+* readout: relative L2 error <= 1e-4 per tile and step;
+* row/column factors and FP16 pivots: bit-exact;
+* codes: bit-exact, except entries whose oracle pre-rounding value lies within 1e-5 of a
+  rounding boundary (x.5); after such a mismatch the oracle continues from the GPU's segment.
+"""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+
+import oracle
+from quantized_delta_rule_amd import synth
+
+BOUNDARY_TOL = 1e-5
+READOUT_TOL = 1e-4
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------------------------------
+# plans (oracle side)
+# ------------------------------------------------------------------------------------------
+
+def omega_from_steps(w, layer, phase, steps):
+    """omega [H, d] = mean over requests and steps of g_i^2 (oracle row impact)."""
+    acc = np.zeros((w.H, w.d))
+    for s in range(steps):
+        x = synth.step_inputs(w, layer, s, phase)
+        a = synth.alpha_rows(w, x["alpha"])
+        for h in range(w.H):
+            acc[h] += oracle.row_impact(x["q"][:, h], x["k"][:, h], a[:, h], x["beta"][:, h])
+    return (acc / steps).astype(np.float32)
+
+
+def measured_distortion(w, omegas, n_req=8, samples=(32, 64)):
+    """KDA d_u(b): per key row, the squared reconstruction error summed over the row, of the
+    uniform-b quantizer without pivots, averaged over calibration states (fp32 runs from zero on
+    the calibration stream, n_req requests, states at the sample steps)."""
+    d, H = w.d, w.H
+    choices = list(w.choices)
+    du = np.zeros((w.layers, H, d, len(choices)))
+    for layer in range(w.layers):
+        S = np.zeros((n_req * H, d, d), np.float32)
+        cnt = 0
+        prev = 0
+        for smp in samples:
+            xs = [synth.step_inputs(w, layer, s, "calib") for s in range(prev, smp)]
+            prev = smp
+            q = np.stack([x["q"][:n_req].reshape(-1, d) for x in xs])
+            k = np.stack([x["k"][:n_req].reshape(-1, d) for x in xs])
+            v = np.stack([x["v"][:n_req].reshape(-1, d) for x in xs])
+            a = np.stack([synth.alpha_rows(w, x["alpha"])[:n_req].reshape(-1, d) for x in xs])
+            be = np.stack([x["beta"][:n_req].reshape(-1) for x in xs])
+            oracle.fp32_run(S, q, k, v, a, be)
+            for t in range(n_req * H):
+                h = t % H
+                for ci, b in enumerate(choices):
+                    head = oracle.Head(np.full(d, b, np.int8), np.zeros(d, np.uint8),
+                                       omegas[layer, h])
+                    Sh, _, _, _ = head.unpack(head.encode(S[t]))
+                    err = (S[t].astype(np.float64) - Sh) ** 2
+                    du[layer, h, :, ci] += err.sum(axis=1)
+            cnt += 1
+        du[layer] /= cnt * n_req
+    return du
+
+
+def oracle_plan(w):
+    """(bits, pivot, omega) each [layers, H, d] for workload w, computed by the oracle."""
+    L_, H, d = w.layers, w.H, w.d
+    phase, nsteps = ("calib", w.calib_steps) if w.calib_steps else ("warmup", w.warmup)
+    omegas = np.stack([omega_from_steps(w, l, phase, nsteps) for l in range(L_)])
+    bits = np.zeros((L_, H, d), np.int8)
+    piv = np.zeros((L_, H, d), np.uint8)
+    if w.alloc == "fixed":
+        for h, b in enumerate(w.fixed_bits):
+            if b == 0:
+                piv[:, h] = 1
+                bits[:, h] = max(w.choices)
+            else:
+                bits[:, h] = b
+        return bits, piv, omegas
+    l_u, s_u = synth.plan_tables(w)
+    Lw = oracle.lifetime_weight(l_u, w.horizon)
+    choices = list(w.choices)
+    if w.du == "synthetic":
+        du = synth.synthetic_distortion(s_u, choices)
+    else:
+        du = measured_distortion(w, omegas).reshape(-1, len(choices))
+    risk = Lw * du[:, -1]
+    pv = oracle.select_pivots(risk, w.n_pivots)
+    keep = np.setdiff1d(np.arange(Lw.size), pv)
+    if w.alloc == "mcdp":
+        cost = Lw[keep, None] * du[keep]
+        b_keep, _ = oracle.mcdp_allocate(cost, choices, w.nominal * keep.size)
+    else:
+        n = np.full(keep.size, float(d))
+        b_keep, _ = oracle.lagrangian_allocate(Lw[keep], du[keep], n, choices,
+                                               w.nominal * float(n.sum()))
+    unit_bits = np.full(Lw.size, max(choices), np.int64)
+    unit_bits[keep] = b_keep
+    unit_piv = np.zeros(Lw.size, np.uint8)
+    unit_piv[pv] = 1
+    if w.kind == "gdn":
+        bits[:] = unit_bits.reshape(L_, H)[:, :, None]
+        piv[:] = unit_piv.reshape(L_, H)[:, :, None]
+    else:
+        bits[:] = unit_bits.reshape(L_, H, d)
+        piv[:] = unit_piv.reshape(L_, H, d)
+    return bits, piv, omegas
+
+
+def warm_state(w, layer, threads=16):
+    """Initial fp32 states [B*H, d, d]: w.warmup unquantized steps from zero (oracle)."""
+    d = w.d
+    S = np.zeros((w.B * w.H, d, d), np.float32)
+    xs = [synth.step_inputs(w, layer, s, "warmup") for s in range(w.warmup)]
+    q = np.stack([x["q"].reshape(-1, d) for x in xs])
+    k = np.stack([x["k"].reshape(-1, d) for x in xs])
+    v = np.stack([x["v"].reshape(-1, d) for x in xs])
+    a = np.stack([synth.alpha_rows(w, x["alpha"]).reshape(-1, d) for x in xs])
+    be = np.stack([x["beta"].reshape(-1) for x in xs])
+    oracle.fp32_run(S, q, k, v, a, be, threads=threads)
+    return S
+
+
+# ------------------------------------------------------------------------------------------
+# comparison
+# ------------------------------------------------------------------------------------------
+
+class Mismatch(AssertionError):
+    pass
+
+
+def compare_segment(head, seg_gpu, seg_orc, pre, where):
+    """Returns the number of allowed boundary mismatches; raises on anything else."""
+    if np.array_equal(seg_gpu, seg_orc):
+        return 0
+    Sg, rg, cg, zg = head.unpack(seg_gpu)
+    So, ro, co, zo = head.unpack(seg_orc)
+    if not np.array_equal(rg, ro):
+        i = np.nonzero(rg != ro)[0]
+        raise Mismatch(f"{where}: row factors differ at rows {i[:8]} gpu {rg[i[:4]]} orc {ro[i[:4]]}")
+    if not np.array_equal(cg, co):
+        j = np.nonzero(cg != co)[0]
+        raise Mismatch(f"{where}: column factors differ at cols {j[:8]} gpu {cg[j[:4]]} orc {co[j[:4]]}")
+    piv = head.pivot.astype(bool)
+    if piv.any() and not np.array_equal(Sg[piv].view(np.uint32), So[piv].view(np.uint32)):
+        raise Mismatch(f"{where}: FP16 pivot rows differ")
+    bad = zg != zo
+    if bad.any():
+        frac = np.abs(np.abs(pre[bad]) - np.floor(np.abs(pre[bad])) - 0.5)
+        if np.any(frac > BOUNDARY_TOL) or np.any(np.abs(zg[bad].astype(int) - zo[bad]) > 1):
+            ii = np.argwhere(bad)[:6]
+            raise Mismatch(f"{where}: codes differ away from a rounding boundary at {ii.tolist()}"
+                           f" gpu {zg[bad][:6]} orc {zo[bad][:6]} pre {pre[bad][:6]}")
+        return int(bad.sum())
+    # codes equal but bytes differ: padding or stray bits
+    raise Mismatch(f"{where}: segments differ outside codes/factors")
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    n = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (n if n > 0 else 1.0))
+
+
+class Tracker:
+    def __init__(self):
+        self.boundary = 0
+        self.worst_readout = 0.0
+        self.steps = 0
+        self.t0 = time.time()
+
+
+# ------------------------------------------------------------------------------------------
+# one-layer run: GPU through the C ABI, oracle on the chosen tiles
+# ------------------------------------------------------------------------------------------
+
+def run_layer(w, layer, bits, piv, om, steps, tiles=None, mode=0, S0=None, check_encode=True,
+              plan=None, pool=None, inputs=None):
+    """Encodes S0 (oracle warm-up unless given) on the GPU, checks the encode against the
+    oracle, then runs `steps` decode steps and checks every step on `tiles` (default: all).
+    Returns (Tracker, plan, pool)."""
+    import torch
+    from quantized_delta_rule_amd import stepq
+
+    d, H, B = w.d, w.H, w.B
+    kind = stepq.GDN if w.kind == "gdn" else stepq.KDA
+    if plan is None:
+        plan = stepq.Plan(kind, bits, piv, om, mode=mode, max_batch=B)
+    heads = [oracle.Head(bits[h], piv[h], om[h]) for h in range(H)]
+    bpr = plan.bytes_per_request
+    segs = [plan.head_segment(h) for h in range(H)]
+    tiles = list(range(B * H)) if tiles is None else list(tiles)
+    dev = torch.device("cuda:0")
+    if S0 is None:
+        S0 = warm_state(w, layer)
+    if pool is None:
+        pool = plan.alloc_pool(B)
+        plan.encode(torch.from_numpy(S0).to(dev), pool, B)
+        torch.cuda.synchronize()
+    tr = Tracker()
+
+    def gpu_seg(host_pool, t):
+        b, h = divmod(t, H)
+        off, n = segs[h]
+        return host_pool[b * bpr + off: b * bpr + off + n]
+
+    seg_o = {}
+    host = pool.cpu().numpy()
+    for t in tiles:
+        h = t % H
+        so, pre, fl = heads[h].encode(S0[t], want_pre=True)
+        if check_encode:
+            tr.boundary += compare_segment(heads[h], gpu_seg(host, t), so, pre,
+                                           f"encode tile {t} (head {h})")
+        seg_o[t] = gpu_seg(host, t).copy() if not check_encode else so
+    for s in range(steps):
+        x = synth.step_inputs(w, layer, s, "decode") if inputs is None else inputs(s)
+        a_rows = synth.alpha_rows(w, x["alpha"])
+        g = {k_: torch.from_numpy(v_).to(dev) for k_, v_ in x.items()}
+        out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+        plan.step(pool, B, g["q"], g["k"], g["v"], g["alpha"], g["beta"], out)
+        if mode == 1:
+            plan.sync()
+        torch.cuda.synchronize()
+        host = pool.cpu().numpy()
+        outh = out.cpu().numpy()
+        for t in tiles:
+            b, h = divmod(t, H)
+            o, S_upd, pre, fl = heads[h].step(seg_o[t], x["q"][b, h], x["k"][b, h],
+                                               x["v"][b, h], a_rows[b, h], x["beta"][b, h],
+                                               want_state=True)
+            err = rel_l2(outh[b, h], o)
+            tr.worst_readout = max(tr.worst_readout, err)
+            if err > READOUT_TOL:
+                raise Mismatch(f"step {s} tile {t}: readout rel L2 {err:.3e}")
+            gs = gpu_seg(host, t)
+            nb = compare_segment(heads[h], gs, seg_o[t], pre, f"step {s} tile {t} (head {h})")
+            if nb:
+                tr.boundary += nb
+                seg_o[t] = gs.copy()  # continue from the GPU's state (teacher forcing)
+        tr.steps += 1
+    return tr, plan, pool
