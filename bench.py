@@ -1,0 +1,251 @@
+"""Decode-step benchmark: head-steps/s and achieved HBM bandwidth of the fused packed-state
+decode step on one MI355X.
+
+Default workload: 70 concurrent requests x 48 GDN heads, d_k = d_v = 128, nominal 6-bit per-head
+map from the multiple-choice DP (widths {4,6,8}, one FP16 pivot head), initial states from 16
+unquantized warm-up steps.  A step is one decode step of the whole batch (one kernel launch over
+3,360 tiles).  The timed loop rotates over pool replicas (independent request batches) whose
+total size exceeds twice the 256 MB Infinity Cache, so the packed state streams from HBM.
+
+Prints one JSON line.  Inputs are synthetic (seeded); nothing is read from disk except the
+optional committed counter summary under profiles/.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "decode head-steps/s + achieved HBM GB/s vs peak, nominal-6-bit GDN state pool"
+COUNTERS = os.path.join(ROOT, "profiles", "gdn6_70x48_counters.json")
+KERNEL_SOURCES = ["quantized_delta_rule_amd/csrc/stepq_device.h",
+                  "quantized_delta_rule_amd/csrc/stepq_k128_gdn.hip",
+                  "quantized_delta_rule_amd/csrc/stepq_internal.h"]
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def warm_state(w, layer, dev):
+    """Initial states [B*H, d, d]: w.warmup unquantized delta-rule steps from zero (workload
+    synthesis with plain torch ops; not the decode path)."""
+    import torch
+    from quantized_delta_rule_amd import synth
+    d = w.d
+    S = torch.zeros((w.B * w.H, d, d), dtype=torch.float32, device=dev)
+    for s in range(w.warmup):
+        x = synth.step_inputs(w, layer, s, "warmup")
+        k = torch.from_numpy(x["k"].reshape(-1, d)).to(dev)
+        v = torch.from_numpy(x["v"].reshape(-1, d)).to(dev)
+        a = torch.from_numpy(synth.alpha_rows(w, x["alpha"]).reshape(-1, d)).to(dev)
+        b = torch.from_numpy(x["beta"].reshape(-1)).to(dev)
+        u = (S * k[:, :, None]).sum(1)                                   # S^T k
+        e = v[:, None, :] - a[:, :, None] * u[:, None, :]                # v - a_i u
+        S = a[:, :, None] * S + (b[:, None] * k)[:, :, None] * e
+    return S
+
+
+def cpu_baseline(w, plan_arrays, S_tiles, budget_s, threads):
+    """The oracle (as it stands) on a bounded sample of tiles of the same workload."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    from quantized_delta_rule_amd import synth
+    bits, piv, om = plan_arrays
+    tiles = list(S_tiles.keys())
+    heads = {h: oracle.Head(bits[0, h], piv[0, h], om[0, h]) for h in {t % w.H for t in tiles}}
+    segs = {t: heads[t % w.H].encode(S_tiles[t]) for t in tiles}
+    x = synth.step_inputs(w, 0, 0, "decode")
+    a_rows = synth.alpha_rows(w, x["alpha"])
+    # calibrate: one step per tile on one thread, then size the run to the budget
+    t0 = time.perf_counter()
+    for t in tiles[:4]:
+        b, h = divmod(t, w.H)
+        heads[h].step(segs[t].copy(), x["q"][b, h], x["k"][b, h], x["v"][b, h], a_rows[b, h],
+                      x["beta"][b, h])
+    per = (time.perf_counter() - t0) / 4
+    steps = max(1, int(budget_s * threads / (per * len(tiles))))
+
+    def work(chunk):
+        for s in range(steps):  # the same inputs every step: this only times the oracle
+            for t in chunk:
+                b, h = divmod(t, w.H)
+                heads[h].step(segs[t], x["q"][b, h], x["k"][b, h], x["v"][b, h],
+                              a_rows[b, h], x["beta"][b, h])
+        return len(chunk) * steps
+
+    chunks = [tiles[i::threads] for i in range(threads)]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        done = sum(ex.map(work, chunks))
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "head-steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(tiles)} tiles of replica 0 (every head), {steps} steps each, "
+                      f"{done} tile-steps in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=600)
+    ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--replicas", type=int, default=12)
+    ap.add_argument("--inputs", type=int, default=4, help="distinct input sets per replica")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode step "
+              "shards by request or head with no cross-GPU traffic, so N GPUs run N copies.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from quantized_delta_rule_amd import planning, stepq, synth
+
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    if w.layers != 1 or w.split:
+        raise SystemExit("bench.py times single-layer fused workloads")
+    print(f"[bench] workload {w.wid} {w.name}: planning", file=sys.stderr, flush=True)
+    bits, piv, om = planning.plan_arrays(w)
+    kind = stepq.GDN if w.kind == "gdn" else stepq.KDA
+    plan = stepq.Plan(kind, bits[0], piv[0], om[0])
+    alg_bytes = planning.algorithmic_bytes(w, plan)
+    R = args.replicas
+    pools, inputs, S_sample = [], [], {}
+    for r in range(R):
+        S0 = warm_state(w, r, dev)
+        pool = plan.alloc_pool(w.B)
+        plan.encode(S0, pool, w.B)
+        if r == 0 and not args.no_cpu:
+            pick = [b * w.H + h for b, h in zip(range(0, w.B, max(1, w.B // w.H)), range(w.H))]
+            S_sample = {t: S0[t].cpu().numpy() for t in pick}
+        del S0
+        pools.append(pool)
+        sets = []
+        for j in range(args.inputs):
+            x = synth.step_inputs(w, r, j, "decode")
+            sets.append({k: torch.from_numpy(v).to(dev) for k, v in x.items()})
+        inputs.append(sets)
+    torch.cuda.synchronize()
+    print(f"[bench] {R} replicas x {plan.bytes_per_request * w.B / 2**20:.1f} MiB pool "
+          f"({plan.bits_per_value:.3f} bits/value), timing", file=sys.stderr, flush=True)
+
+    out = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device=dev)
+    L = stepq.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.c_void_p
+    calls = []
+    for r in range(R):
+        for j in range(args.inputs):
+            x = inputs[r][j]
+            calls.append((plan._h, P(pools[r].data_ptr()), w.B, P(x["q"].data_ptr()),
+                          P(x["k"].data_ptr()), P(x["v"].data_ptr()), P(x["alpha"].data_ptr()),
+                          P(x["beta"].data_ptr()), P(out.data_ptr()), stream))
+    # order: replica-major rotation so consecutive steps touch different pools
+    order = [calls[(i % R) * args.inputs + (i // R) % args.inputs] for i in range(len(calls))]
+    step_fn = L.stepq_decode_step
+
+    for i in range(args.warmup):
+        rc = step_fn(*order[i % len(order)])
+        if rc:
+            raise RuntimeError(L.stepq_last_error().decode())
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        step_fn(*order[i % len(order)])
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    if plan.status() != 0:
+        raise RuntimeError("status flags raised during the benchmark")
+
+    # cache-hot reference: one pool stepped repeatedly (labelled, not the headline)
+    hot = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(50)]
+    for a, b in hot:
+        a.record()
+        step_fn(*order[0])
+        b.record()
+    torch.cuda.synchronize()
+    hot_ms = float(np.median([a.elapsed_time(b) for a, b in hot]))
+
+    if args.copy_calib:
+        src = torch.empty(2 ** 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    ms_per_step = wall * 1e3 / args.steps
+    avg_k = float(k_ms.mean())
+    heads = w.B * w.H * w.layers
+    achieved = alg_bytes / (avg_k * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS):
+        c = json.load(open(COUNTERS))
+        if c.get("kernel_sha") == kernel_sha():
+            traffic = c["hbm_bytes_per_launch"]
+    res = {
+        "metric": METRIC,
+        "value": heads / (ms_per_step * 1e-3),
+        "unit": "head-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.B} requests x {w.H} GDN heads, d_k=d_v={w.d}, nominal "
+                        f"{w.nominal}-bit MC-DP map {w.choices} + {w.n_pivots} FP16 pivot head, "
+                        f"{R} rotating pool replicas",
+            "bits_per_value": round(plan.bits_per_value, 4),
+            "pool_mib_per_replica": round(plan.bytes_per_request * w.B / 2 ** 20, 2),
+            "algorithmic_bytes_per_step": alg_bytes,
+            "kernel_ms_mean": avg_k,
+            "kernel_ms_p10_p50_p90": [float(np.percentile(k_ms, p)) for p in (10, 50, 90)],
+            "cache_hot_single_pool_kernel_ms": hot_ms,
+            "cache_hot_single_pool_GBps": alg_bytes / (hot_ms * 1e-3) / 1e9,
+        },
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "k_gdn<128, FUSED>", "kernel_sha": kernel_sha()},
+    }
+    if not args.no_cpu and S_sample:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        print(f"[bench] CPU oracle baseline ({threads} threads, ~{args.cpu_seconds:.0f} s)",
+              file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, (bits, piv, om), S_sample, args.cpu_seconds,
+                                           threads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
