@@ -143,7 +143,7 @@ class Head:
     def encode(self, S, want_pre=False):
         S = _c(S, np.float32)
         seg = np.zeros(self.seg_bytes, np.uint8)
-        pre = np.empty(self.dk * self.dv, np.float32) if want_pre else None
+        pre = np.empty(self.dk * self.dv, np.float64) if want_pre else None
         fl = ctypes.c_uint32(0)
         lib().orc_encode(self.dk, self.dv, _p(self.bits), _p(self.pivot), _p(self.omega),
                          _p(S), _p(seg), _p(pre), ctypes.addressof(fl))
@@ -167,7 +167,7 @@ class Head:
         a = _c(np.broadcast_to(np.asarray(a, np.float32), (self.dk,)), np.float32)
         out = np.empty(self.dv, np.float32)
         S = np.empty(self.dk * self.dv, np.float32) if want_state else None
-        pre = np.empty(self.dk * self.dv, np.float32) if want_state else None
+        pre = np.empty(self.dk * self.dv, np.float64) if want_state else None
         fl = ctypes.c_uint32(0)
         rc = lib().orc_tile_step(self.dk, self.dv, _p(self.bits), _p(self.pivot),
                                  _p(self.omega), _p(seg), _p(q), _p(k), _p(v), _p(a),

@@ -23,8 +23,9 @@
  * readings this build takes where the pages leave the step open.
  *
  * Arithmetic: IEEE binary32, round to nearest even, subnormals kept.  Every operation is rounded
- * on its own; a fused multiply-add appears only where fmaf() is written.  Build with
- * -ffp-contract=off and without -ffast-math.  Sums run in a fixed order:
+ * on its own; a fused multiply-add appears only where fmaf() is written.  A code is the
+ * round-half-even integer of the exact product y * (1/c) (no intermediate rounding of the
+ * product).  Build with -ffp-contract=off and without -ffast-math.  Sums run in a fixed order:
  *   tree(x_0..x_{n-1})  pairwise: tree(first half) + tree(second half); tree(x) = x.
  *   dot(x, y)           aligned groups of four terms are accumulated first to last with
  *                       fused multiply-adds, and the group sums are combined by tree().
@@ -113,9 +114,11 @@ float orc_dot(const float* x, const float* y, int n) { return dot_fixed(x, 1, y,
 
 static float rcp0(float x) { return x == 0.0f ? 0.0f : 1.0f / x; }
 
-static float rne(float x) { return nearbyintf(x); } /* default rounding mode: ties to even */
+/* round half to even of the exact product a*b (binary32 operands: the product is exact in
+   binary64), as a binary64 value */
+static double rne_prod(float a, float b) { return nearbyint((double)a * (double)b); }
 
-static float clampf(float x, float lo, float hi) { return x < lo ? lo : (x > hi ? hi : x); }
+static double clampd(double x, double lo, double hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 /* ------------------------------------------------------------------------------------------ */
 /* packed segment layout of one head                                                          */
@@ -264,9 +267,10 @@ void orc_row_den(int dk, const float* omega, float* den) {
 }
 
 /* Encode the fp32 state S (dk x dv row-major) into seg.  pre (optional, dk*dv) receives the
-   final pre-rounding value y_ij * (1/c_j) of every quantized entry (0 elsewhere). */
+   final pre-rounding value y_ij * (1/c_j) (exact, binary64) of every quantized entry (0
+   elsewhere). */
 int orc_encode(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const float* omega,
-               const float* S, uint8_t* seg, float* pre, uint32_t* flags) {
+               const float* S, uint8_t* seg, double* pre, uint32_t* flags) {
   seg_layout s = layout_of(dk, dv, bits, pivot);
   uint32_t fl = 0;
   float* den = (float*)malloc(sizeof(float) * dk);
@@ -322,14 +326,15 @@ int orc_encode(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const f
     }
     c0[j] = mx;
   }
-  /* first quantization with c0, then the omega-weighted least-squares column refit:
+  /* first quantization with c0 (its clamp never binds: |y| / qmax <= c0), then the
+     omega-weighted least-squares column refit:
      c1_j = argmin_c sum_i omega_i (S_ij - r_i c z0_ij)^2
           = sum_i W_i z0_ij y_ij / sum_i W_i z0_ij^2   with W_i = omega_i r_i^2, y = S / r */
   for (int j = 0; j < dv; j++) {
     float ic0 = rcp0(c0[j]);
     for (int i = 0; i < dk; i++) {
       long e = (long)i * dv + j;
-      z0[e] = clampf(rne(y[e] * ic0), -qmax[i], qmax[i]);
+      z0[e] = (float)clampd(rne_prod(y[e], ic0), -qmax[i], qmax[i]);
       a[e] = W[i] * z0[e];
     }
     float num = dot_fixed(a + j, dv, y + j, dv, dk);
@@ -345,9 +350,8 @@ int orc_encode(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const f
     if (pivot[i]) continue;
     for (int j = 0; j < dv; j++) {
       long e = (long)i * dv + j;
-      float t = y[e] * ic[j];
-      if (pre) pre[e] = t;
-      float zr = clampf(rne(t), -qmax[i], qmax[i]);
+      if (pre) pre[e] = (double)y[e] * (double)ic[j];
+      double zr = clampd(rne_prod(y[e], ic[j]), -qmax[i], qmax[i]);
       int zi = zr == zr ? (int)zr : 0; /* NaN only follows a non-finite state (flagged) */
       put_code(&s, seg, bits, i, j, zi);
     }
@@ -392,7 +396,7 @@ static void delta_update_readout(int dk, int dv, float* S, const float* q, const
    the final pre-rounding values.  Returns 0, or -1 on a corrupt code. */
 int orc_tile_step(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const float* omega,
                   uint8_t* seg, const float* q, const float* k, const float* v, const float* a,
-                  float beta, float* out, float* S_upd, float* pre, uint32_t* flags) {
+                  float beta, float* out, float* S_upd, double* pre, uint32_t* flags) {
   float* S = (float*)malloc(sizeof(float) * dk * dv);
   int rc = orc_unpack(dk, dv, bits, pivot, seg, S, NULL, NULL, NULL);
   delta_update_readout(dk, dv, S, q, k, v, a, beta, out);
