@@ -11,20 +11,23 @@
 //   Background: S_t = A_t S_{t-1} + beta k v^T with A_t = Diag(a)(I - beta k k^T).
 //
 // Work mapping (one workgroup per (request, head) tile, d = d_k = d_v in {64, 128}):
-//   wave w owns rows 64w .. 64w+63, lane L owns the G = d/64 columns G*L .. G*L+G-1.  The tile
-//   lives in VGPRs (64*G floats per lane).  Every reduction over rows (k^T S, q^T S, the column
-//   maximum, the least-squares sums) runs inside a lane, the two waves of a d = 128 tile adding
-//   their halves through LDS.  The one reduction over columns (the row's mean magnitude) goes
-//   through an LDS transpose inside the wave, after which lane L owns row 64w + L.  Per-row
-//   scalars are read from LDS at wave-uniform addresses (broadcast reads, no VALU work).
+//   d/32 waves; wave w owns rows 32w .. 32w+31, lane L owns the G = d/64 columns
+//   G*L .. G*L+G-1.  The tile lives in VGPRs (32*G floats per lane).  Every reduction over rows
+//   (k^T S, q^T S, the column maximum, the least-squares sums) runs inside a lane, the waves
+//   adding their partials through LDS as a pairwise tree.  The one reduction over columns (the
+//   row's mean magnitude) goes through an LDS transpose inside the wave, after which lanes L and
+//   L+32 own row 32w + L (one half of the columns each).  Per-row scalars are read from LDS at
+//   wave-uniform addresses (broadcast reads, no VALU work).
 //
 // Arithmetic matches a fixed binary32 evaluation order bit for bit:
 //   dequant  S_hat = r_i c_j z_ij rounded once (c_j z_ij is exact)
 //   update   e = fma(-a_i, u_j, v_j);  S = fma(a_i, S_hat, (beta k_i) e)
 //   sums     aligned groups of 4 rows accumulated with fma first to last, the group sums then
 //            added as a pairwise tree; the row magnitude sum is a pairwise tree over columns
-//   rounding round-half-even; x + 1.5*2^23 leaves rne(x) in the low mantissa bits, whose low b
-//            bits are then the two's-complement code.
+//   codes    round-half-even of the exact product y * (1/c): fma(y, 1/c, 1.5*2^23) rounds the
+//            exact product once onto the integer grid of [2^23, 2^24); the low b bits of that
+//            float are the two's-complement code, and the clamp to +-qmax is applied in the same
+//            offset domain.
 // The build passes -ffp-contract=off: no multiply-add is fused unless written as fmaf.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -58,13 +61,22 @@ __device__ __forceinline__ float h2f(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-__device__ __forceinline__ uint16_t f2h(float x) {  // v_cvt_f16_f32: nearest even, IEEE mode
+// binary32 -> binary16, nearest even (v_cvt_f16_f32).  The empty asm pins x as a rounded binary32
+// value: without it the compiler may fold a producing fma into v_fma_mix{lo,hi}_f16, which
+// rounds the exact fma result straight to binary16 and differs on binary16 ties.
+__device__ __forceinline__ uint16_t f2h(float x) {
+  asm volatile("" : "+v"(x));
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
 __device__ __forceinline__ float rcp0(float x) { return x == 0.0f ? 0.0f : 1.0f / x; }
 
 __device__ __forceinline__ bool is_inf16(uint16_t h) { return (h & 0x7FFFu) == 0x7C00u; }
+
+// code offset by kMagic: fma rounds the exact product y*ic once; then clamp to +-qm
+__device__ __forceinline__ float quant_off(float y, float ic, float qm) {
+  return __builtin_amdgcn_fmed3f(__builtin_fmaf(y, ic, kMagic), kMagic - qm, kMagic + qm);
+}
 
 // Visibility of this wave's own LDS writes to its other lanes (no s_barrier needed).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -84,15 +96,47 @@ __device__ __forceinline__ void tree_push(float* lv, float x) {
   }
 }
 
+// Tile geometry: d/32 waves of 32 rows; lane L owns the G = d/64 columns G*L .. G*L+G-1.
+template <int D>
+struct Geo {
+  static constexpr int G = D / 64;    // columns per lane
+  static constexpr int R = 32;        // rows per wave
+  static constexpr int NW = D / R;    // waves per tile
+  static constexpr int NT = 64 * NW;  // threads per tile
+  static constexpr int NQ = R / 4;    // fma chains of four per column and wave
+  static constexpr int TOP = 3;       // tree level holding a wave's partial (log2 NQ)
+};
+
+// Per-row records, read at wave-uniform addresses (broadcast reads).
+struct RowA { float r, k, a, bk; };   // decode, u, update
+struct RowB { float q, ir, W, iq; };  // readout, row factor, least squares, column maximum
+
 template <int D>
 struct Smem {
-  static constexpr int NW = D / 64;
-  float r[D], k[D], bk[D], q[D], a[D], ir[D], W[D], iq[D], qm[D];
-  float red[2][NW][D];
+  static constexpr int NW = Geo<D>::NW;
+  RowA ra[D];
+  RowB rb[D];
+  float qm[D];
+  float red[3][NW][D];
   union {
-    float absT[NW][64][65];                    // [wave][row][lane], +1 pad: conflict-free
+    float absT[NW][32][65];                    // [wave][row][lane], +1 pad: conflict-free
     uint32_t code[(2 * D * 8 / 32 + 1) * 64];  // mixed-width tiles: code block staging
   };
+};
+
+// Wave-local views: the base index comes from threadIdx, so it stays in a VGPR and every
+// per-row read is one ds_read with an immediate offset.
+template <int D>
+struct Rows {
+  const RowA* ra;
+  const RowB* rb;
+  const float* qm;
+  __device__ __forceinline__ Rows(const Smem<D>& sm) {
+    const int base = (threadIdx.x >> 6) * 32;
+    ra = sm.ra + base;
+    rb = sm.rb + base;
+    qm = sm.qm + base;
+  }
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -128,75 +172,200 @@ __device__ __forceinline__ void put_code(uint32_t& acc, uint32_t f, Store&& stor
   }
 }
 
-__device__ __forceinline__ void raise_flags(const StepArgs& A, unsigned fl) {
+template <typename Args>
+__device__ __forceinline__ void raise_flags(const Args& A, unsigned fl) {
   if (fl) atomicOr(A.P.status, fl);
 }
 
 // ---------------------------------------------------------------------------------------------
-// shared phases
+// phases shared by the tile variants (S: this lane's 32 rows x G columns)
 // ---------------------------------------------------------------------------------------------
 
-// Row factor of row trow (one lane per row) from this wave's transposed |S| partials.  Writes
-// r_hat to the pool (unless rblk is null) and ir = 1/r_hat (0 if dead or pivot) and
-// W = (omega r_hat) r_hat (0 likewise) to LDS.
+// dot over the wave's 32 rows of a per-row scalar x_r with S[r][g]: fma chains of four, then a
+// pairwise tree over the 8 chains.
+template <int G, typename XF>
+__device__ __forceinline__ void row_dot(const float (&S)[32][G], XF&& xr, float* res) {
+  float lv[G][4];
+  sfor<8>([&](auto mm) {
+    constexpr int m = CI(mm);
+    const float x0 = xr(4 * m), x1 = xr(4 * m + 1), x2 = xr(4 * m + 2), x3 = xr(4 * m + 3);
+    sfor<G>([&](auto gg) {
+      constexpr int g = CI(gg);
+      float s = x0 * S[4 * m][g];
+      s = __builtin_fmaf(x1, S[4 * m + 1][g], s);
+      s = __builtin_fmaf(x2, S[4 * m + 2][g], s);
+      s = __builtin_fmaf(x3, S[4 * m + 3][g], s);
+      tree_push<m>(lv[g], s);
+    });
+  });
+  sfor<G>([&](auto gg) { res[CI(gg)] = lv[CI(gg)][3]; });
+}
+
+// Cross-wave combination of this lane's per-wave partials (red[slot][w][col]).
 template <int D>
-__device__ __forceinline__ void row_factor(Smem<D>& sm, int w, int lane, int trow, float den,
-                                           float om, bool piv, uint16_t* rblk, unsigned& fl) {
-  float lv[7];
-  const float* src = &sm.absT[w][lane][0];
-  sfor<64>([&](auto jj) { tree_push<CI(jj)>(lv, src[CI(jj)]); });
-  const float m = lv[6] * (1.0f / (float)D);
+__device__ __forceinline__ void xwave_put(Smem<D>& sm, int slot, int w, int lane,
+                                          const float* x) {
+  constexpr int G = Geo<D>::G;
+  sfor<G>([&](auto gg) { sm.red[slot][w][G * lane + CI(gg)] = x[CI(gg)]; });
+}
+// pairwise tree over the waves' partials (rows 0-31, 32-63, ...)
+template <int D>
+__device__ __forceinline__ void xwave_sum(Smem<D>& sm, int slot, int lane, float* x) {
+  constexpr int G = Geo<D>::G, NW = Geo<D>::NW;
+  sfor<G>([&](auto gg) {
+    const int c = G * lane + CI(gg);
+    if constexpr (NW == 2) {
+      x[CI(gg)] = sm.red[slot][0][c] + sm.red[slot][1][c];
+    } else {
+      x[CI(gg)] = (sm.red[slot][0][c] + sm.red[slot][1][c]) +
+                  (sm.red[slot][2][c] + sm.red[slot][3][c]);
+    }
+  });
+}
+template <int D>
+__device__ __forceinline__ void xwave_max(Smem<D>& sm, int slot, int lane, float* x) {
+  constexpr int G = Geo<D>::G, NW = Geo<D>::NW;
+  sfor<G>([&](auto gg) {
+    const int c = G * lane + CI(gg);
+    float m = sm.red[slot][0][c];
+    sfor<NW - 1>([&](auto ww) { m = __builtin_fmaxf(m, sm.red[slot][CI(ww) + 1][c]); });
+    x[CI(gg)] = m;
+  });
+}
+
+// |S| partial sums of each row over this lane's columns, transposed through LDS.
+template <int D>
+__device__ __forceinline__ void put_rowabs(Smem<D>& sm, const float (&S)[32][Geo<D>::G],
+                                           int lane) {
+  constexpr int G = Geo<D>::G;
+  float* dst = &sm.absT[0][0][0] + (threadIdx.x >> 6) * (32 * 65) + lane;
+  sfor<32>([&](auto rr) {
+    constexpr int r = CI(rr);
+    float a;
+    if constexpr (G == 2) a = __builtin_fabsf(S[r][0]) + __builtin_fabsf(S[r][1]);
+    else a = __builtin_fabsf(S[r][0]);
+    dst[r * 65] = a;
+  });
+}
+
+// Row factor of row 32w + (lane & 31): lanes L and L+32 each sum half of the row's columns, the
+// halves are added, and lane L < 32 writes r_hat to the pool (unless rblk is null) and
+// ir = 1/r_hat (0 if dead or pivot) and W = (omega r_hat) r_hat (0 likewise) into the row
+// record.
+template <int D>
+__device__ __forceinline__ void row_factor(Smem<D>& sm, int lane, int row, float den, float om,
+                                           bool piv, uint16_t* rblk, unsigned& fl) {
+  float lv[6];
+  const float* src =
+      &sm.absT[0][0][0] + (threadIdx.x >> 6) * (32 * 65) + (lane & 31) * 65 + (lane & 32);
+  sfor<32>([&](auto jj) { tree_push<CI(jj)>(lv, src[CI(jj)]); });
+  const float other = __shfl_xor(lv[5], 32);
+  const float m = (lane < 32 ? lv[5] + other : other + lv[5]) * (1.0f / (float)D);
   if (!__builtin_isfinite(m)) fl |= kFlagNonfinite;
+  if (lane >= 32) return;
   if (piv) {
-    sm.ir[trow] = 0.0f;
-    sm.W[trow] = 0.0f;
-    if (rblk) rblk[trow] = 0;
+    sm.rb[row].ir = 0.0f;
+    sm.rb[row].W = 0.0f;
+    if (rblk) rblk[row] = 0;
     return;
   }
   const float r = (m + 1e-8f) / den;
   const uint16_t rh = f2h(r);
   if (is_inf16(rh)) fl |= kFlagScaleOvf;
-  if (rblk) rblk[trow] = rh;
+  if (rblk) rblk[row] = rh;
   const float rf = h2f(rh);
-  sm.ir[trow] = rcp0(rf);
-  sm.W[trow] = (om * rf) * rf;
+  sm.rb[row].ir = rcp0(rf);
+  sm.rb[row].W = (om * rf) * rf;
 }
 
-// Adds the per-wave partials of this lane's columns across waves: red[slot][w][col].
-template <int D, int G>
-__device__ __forceinline__ void xwave_sum(Smem<D>& sm, int slot, int lane, float* x) {
-  if constexpr (D / 64 > 1) {
+// y = S * ir (in place) and the column maximum max_i |y| (GDN: one width, the 1/qmax factor
+// is applied after the maximum -- rounding is monotone) or max_i |y| / qmax_i (KDA).
+template <int G, bool KDA>
+__device__ __forceinline__ void scale_rows(float (&S)[32][G], const RowB* rb, float* mx) {
+  sfor<G>([&](auto gg) { mx[CI(gg)] = 0.0f; });
+  sfor<32>([&](auto rr) {
+    constexpr int r = CI(rr);
+    const float ir = rb[r].ir;
+    float iq = 0.0f;
+    if constexpr (KDA) iq = rb[r].iq;
     sfor<G>([&](auto gg) {
-      x[CI(gg)] = sm.red[slot][0][G * lane + CI(gg)] + sm.red[slot][1][G * lane + CI(gg)];
+      constexpr int g = CI(gg);
+      S[r][g] = S[r][g] * ir;
+      if constexpr (KDA) mx[g] = __builtin_fmaxf(mx[g], __builtin_fabsf(S[r][g]) * iq);
+      else mx[g] = __builtin_fmaxf(mx[g], __builtin_fabsf(S[r][g]));
     });
-  }
+  });
 }
 
-// Stages per-wave partials for xwave_sum (caller then __syncthreads()).
-template <int D, int G>
-__device__ __forceinline__ void xwave_put(Smem<D>& sm, int slot, int w, int lane,
-                                          const float* x) {
-  if constexpr (D / 64 > 1) {
-    sfor<G>([&](auto gg) { sm.red[slot][w][G * lane + CI(gg)] = x[CI(gg)]; });
-  }
+// First quantization z0 = rne(y / c0) and the sums of the omega-weighted least-squares fit:
+// num = sum_i (W_i z0) y, sq = sum_i (W_i z0) z0, both as fma chains of four + pairwise tree.
+template <int G>
+__device__ __forceinline__ void ls_sums(const float (&S)[32][G], const RowB* rb, const float* ic0,
+                                        float* num, float* sq) {
+  float ln[G][4], ls[G][4];
+  sfor<8>([&](auto mm) {
+    constexpr int m = CI(mm);
+    float W4[4];
+    sfor<4>([&](auto tt) { W4[CI(tt)] = rb[4 * m + CI(tt)].W; });
+    sfor<G>([&](auto gg) {
+      constexpr int g = CI(gg);
+      float sn = 0.0f, sqv = 0.0f;
+      sfor<4>([&](auto tt) {
+        constexpr int r = 4 * m + CI(tt);
+        const float z0 = __builtin_fmaf(S[r][g], ic0[g], kMagic) - kMagic;  // |z0| <= qmax
+        const float a = W4[CI(tt)] * z0;
+        if constexpr (CI(tt) == 0) {
+          sn = a * S[r][g];
+          sqv = a * z0;
+        } else {
+          sn = __builtin_fmaf(a, S[r][g], sn);
+          sqv = __builtin_fmaf(a, z0, sqv);
+        }
+      });
+      tree_push<m>(ln[g], sn);
+      tree_push<m>(ls[g], sqv);
+    });
+  });
+  sfor<G>([&](auto gg) {
+    num[CI(gg)] = ln[CI(gg)][3];
+    sq[CI(gg)] = ls[CI(gg)][3];
+  });
 }
 
-// Readout out = S^T q for this lane's columns (wave 0 stores).
-template <int D, int G>
+// Column factor from the least-squares sums; wave 0 stores it; returns 1/c_hat (0 if dead).
+template <int G>
+__device__ __forceinline__ void col_factor(const float* num, const float* sq, const float* c0,
+                                           int w, int lane, uint16_t* cblk, float* ic,
+                                           unsigned& fl) {
+  sfor<G>([&](auto gg) {
+    constexpr int g = CI(gg);
+    const float c1 = sq[g] > 0.0f ? num[g] / sq[g] : c0[g];
+    const uint16_t ch = f2h(c1);
+    if (is_inf16(ch)) fl |= kFlagScaleOvf;
+    if (w == 0) cblk[G * lane + g] = ch;
+    ic[g] = rcp0(h2f(ch));
+  });
+}
+
+template <int D>
 __device__ __forceinline__ void store_out(const StepArgs& A, long long tile, int w, int lane,
                                           const float* o) {
+  constexpr int G = Geo<D>::G;
   if (w == 0) sfor<G>([&](auto gg) { A.out[tile * D + G * lane + CI(gg)] = o[CI(gg)]; });
 }
 
-// Split-mode hand-over of the update factors: a (GDN: a[0] = alpha), beta k, and e (GDN) or
-// u and v (KDA) per column.
-template <int D, int G, bool KDA>
+// Split-mode hand-over of the update factors: a_i, beta k_i per row (lane L < 32 of each
+// wave); e_j (GDN) or u_j and v_j (KDA) per column (wave 0).
+template <int D, bool KDA>
 __device__ __forceinline__ void put_stash(const StepArgs& A, long long tile, int w, int lane,
-                                          int trow, float a_row, float bk_row, const float* e,
+                                          int row, float a_row, float bk_row, const float* e,
                                           const float* u, const float* vv) {
+  constexpr int G = Geo<D>::G;
   float* st = A.stash + tile * 4 * D;
-  st[trow] = a_row;
-  st[D + trow] = bk_row;
+  if (lane < 32) {
+    st[row] = a_row;
+    st[D + row] = bk_row;
+  }
   if (w == 0) {
     sfor<G>([&](auto gg) {
       constexpr int g = CI(gg);
@@ -210,31 +379,86 @@ __device__ __forceinline__ void put_stash(const StepArgs& A, long long tile, int
   }
 }
 
+template <int D>
+__device__ __forceinline__ void load_state(const StepArgs& A, long long tile, int row0, int lane,
+                                           float (&S)[32][Geo<D>::G]) {
+  constexpr int G = Geo<D>::G;
+  const float* src = A.S_in + tile * D * D;
+  sfor<32>([&](auto rr) {
+    sfor<G>([&](auto gg) { S[CI(rr)][CI(gg)] = src[(row0 + CI(rr)) * D + G * lane + CI(gg)]; });
+  });
+}
+
+// Per-tile inputs of a step: row records (lanes 0..31 of each wave fill their wave's rows),
+// per-column v or the hand-over.  Returns alpha (GDN) and fills vv / e / u.
+template <int D, int MODE, bool KDA>
+__device__ __forceinline__ void load_inputs(const StepArgs& A, Smem<D>& sm, long long tile,
+                                            int lane, int row, const uint16_t* rblk,
+                                            float& alpha, float* vv, float* e, float* u) {
+  constexpr int G = Geo<D>::G;
+  constexpr bool kRead = MODE == FUSED || MODE == READ;
+  if constexpr (kRead) {
+    sfor<G>([&](auto gg) { vv[CI(gg)] = A.v[tile * D + G * lane + CI(gg)]; });
+    if constexpr (!KDA) alpha = A.alpha[tile];
+  }
+  if constexpr (MODE == WRITE) {
+    const float* st = A.stash + tile * 4 * D;
+    if constexpr (KDA) {
+      sfor<G>([&](auto gg) {
+        u[CI(gg)] = st[2 * D + G * lane + CI(gg)];
+        vv[CI(gg)] = st[3 * D + G * lane + CI(gg)];
+      });
+    } else {
+      alpha = st[0];
+      sfor<G>([&](auto gg) { e[CI(gg)] = st[2 * D + G * lane + CI(gg)]; });
+    }
+  }
+  if (lane < 32) {
+    RowA ra{};
+    if (rblk) ra.r = h2f(rblk[row]);
+    if constexpr (kRead) {
+      const float beta = A.beta[tile];
+      const float kk = A.k[tile * D + row];
+      ra.k = kk;
+      ra.bk = beta * kk;
+      ra.a = KDA ? A.alpha[tile * D + row] : alpha;
+      sm.rb[row].q = A.q[tile * D + row];
+    }
+    if constexpr (MODE == WRITE) {
+      const float* st = A.stash + tile * 4 * D;
+      ra.a = st[row];
+      ra.bk = st[D + row];
+    }
+    sm.ra[row] = ra;
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // GDN: a whole head at one width
 // ---------------------------------------------------------------------------------------------
 
 template <int D, int MODE, int BITS>
 __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, Smem<D>& sm) {
-  constexpr int G = D / 64, R = 64, NQ = R / 4;
+  using Gm = Geo<D>;
+  constexpr int G = Gm::G, R = Gm::R;
   constexpr int WPW = R * G * BITS / 32;  // code words per lane for one wave's rows
   constexpr float QM = (float)((1 << (BITS - 1)) - 1);
   constexpr float IQ = 1.0f / QM;
   constexpr bool kRead = MODE == FUSED || MODE == READ;   // computes u and the readout
   constexpr bool kWrite = MODE != READ;                   // refits and packs
-  const int lane = threadIdx.x & 63, w = wave_id(), trow = threadIdx.x, row0 = w * R;
+  const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
   const long long tile = (long long)b * A.P.H + h;
   uint8_t* seg = A.pool + (long long)b * A.P.bpr + A.P.head_off[h];
   uint32_t* words = reinterpret_cast<uint32_t*>(seg);
   uint16_t* rblk = reinterpret_cast<uint16_t*>(seg + A.P.off_r[h]);
   uint16_t* cblk = reinterpret_cast<uint16_t*>(seg + A.P.off_c[h]);
-  const int prow = h * D + trow;
+  const Rows<D> rows(sm);
   unsigned fl = 0;
 
   float S[R][G];
   float e[G], u[G], vv[G], cc[G];
-  uint32_t wd[WPW > 0 ? WPW : 1];
-  float alpha = 0.0f, beta = 0.0f, den = 1.0f, om = 0.0f, kk = 0.0f;
+  uint32_t wd[WPW];
+  float alpha = 0.0f;
 
   // ---- phase 0: code loads first (they stream from HBM), then the small per-tile inputs
   if constexpr (MODE != ENCODE) {
@@ -242,203 +466,94 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, Smem<D
       wd[CI(xx)] = __builtin_nontemporal_load(&words[(w * WPW + CI(xx)) * 64 + lane]);
     });
     sfor<G>([&](auto gg) { cc[CI(gg)] = h2f(cblk[G * lane + CI(gg)]); });
-    sm.r[trow] = h2f(rblk[trow]);
   }
-  if constexpr (kRead) {
-    alpha = A.alpha[tile];
-    beta = A.beta[tile];
-    kk = A.k[tile * D + trow];
-    sm.k[trow] = kk;
-    sm.bk[trow] = beta * kk;
-    sm.q[trow] = A.q[tile * D + trow];
-    sfor<G>([&](auto gg) { vv[CI(gg)] = A.v[tile * D + G * lane + CI(gg)]; });
-  }
-  if constexpr (MODE == WRITE) {
-    const float* st = A.stash + tile * 4 * D;
-    alpha = st[0];
-    sm.bk[trow] = st[D + trow];
-    sfor<G>([&](auto gg) { e[CI(gg)] = st[2 * D + G * lane + CI(gg)]; });
-  }
+  load_inputs<D, MODE, false>(A, sm, tile, lane, row, MODE != ENCODE ? rblk : nullptr, alpha,
+                              vv, e, u);
+  float den = 1.0f, om = 0.0f;
   if constexpr (kWrite) {
-    den = A.P.den[prow];
-    om = A.P.omega[prow];
+    den = A.P.den[h * D + row];
+    om = A.P.omega[h * D + row];
   }
   wave_lds_sync();
 
-  // ---- phase 1: dequantize, and u = S_hat^T k
   if constexpr (MODE == ENCODE) {
-    const float* src = A.S_in + tile * D * D;
-    sfor<R>([&](auto rr) {
-      sfor<G>([&](auto gg) { S[CI(rr)][CI(gg)] = src[(row0 + CI(rr)) * D + G * lane + CI(gg)]; });
-    });
+    load_state<D>(A, tile, row0, lane, S);
   } else {
-    float lv[G][5];
-    sfor<NQ>([&](auto mm) {
-      constexpr int m = CI(mm);
-      sfor<4>([&](auto tt) {
-        constexpr int r = 4 * m + CI(tt);
-        const float rh = sm.r[row0 + r];
-        sfor<G>([&](auto gg) {
-          constexpr int g = CI(gg);
-          S[r][g] = rh * (cc[g] * (float)get_code<BITS, r * G + g>(wd));
-        });
+    // ---- phase 1: dequantize, and u = S_hat^T k
+    sfor<R>([&](auto rr) {
+      constexpr int r = CI(rr);
+      const float rh = rows.ra[r].r;
+      sfor<G>([&](auto gg) {
+        constexpr int g = CI(gg);
+        S[r][g] = rh * (cc[g] * (float)get_code<BITS, r * G + g>(wd));
       });
-      if constexpr (kRead) {
-        const float k0 = sm.k[row0 + 4 * m], k1 = sm.k[row0 + 4 * m + 1];
-        const float k2 = sm.k[row0 + 4 * m + 2], k3 = sm.k[row0 + 4 * m + 3];
-        sfor<G>([&](auto gg) {
-          constexpr int g = CI(gg);
-          float s = k0 * S[4 * m][g];
-          s = __builtin_fmaf(k1, S[4 * m + 1][g], s);
-          s = __builtin_fmaf(k2, S[4 * m + 2][g], s);
-          s = __builtin_fmaf(k3, S[4 * m + 3][g], s);
-          tree_push<m>(lv[g], s);
-        });
-      }
     });
     if constexpr (kRead) {
-      sfor<G>([&](auto gg) { u[CI(gg)] = lv[CI(gg)][4]; });
-      xwave_put<D, G>(sm, 0, w, lane, u);
+      row_dot<G>(S, [&](int r) { return rows.ra[r].k; }, u);
+      xwave_put<D>(sm, 0, w, lane, u);
       __syncthreads();
-      xwave_sum<D, G>(sm, 0, lane, u);
+      xwave_sum<D>(sm, 0, lane, u);
       sfor<G>([&](auto gg) { e[CI(gg)] = __builtin_fmaf(-alpha, u[CI(gg)], vv[CI(gg)]); });
     }
-  }
 
-  // ---- phase 2: gated delta update, readout, row magnitudes
-  if constexpr (MODE != ENCODE) {
-    float lv[G][5];
-    sfor<NQ>([&](auto mm) {
-      constexpr int m = CI(mm);
-      sfor<4>([&](auto tt) {
-        constexpr int r = 4 * m + CI(tt);
-        const float bk = sm.bk[row0 + r];
-        sfor<G>([&](auto gg) {
-          constexpr int g = CI(gg);
-          S[r][g] = __builtin_fmaf(alpha, S[r][g], bk * e[g]);
-        });
+    // ---- phase 2: gated delta update and readout
+    sfor<R>([&](auto rr) {
+      constexpr int r = CI(rr);
+      const float bk = rows.ra[r].bk;
+      sfor<G>([&](auto gg) {
+        S[r][CI(gg)] = __builtin_fmaf(alpha, S[r][CI(gg)], bk * e[CI(gg)]);
       });
-      if constexpr (kRead) {
-        const float q0 = sm.q[row0 + 4 * m], q1 = sm.q[row0 + 4 * m + 1];
-        const float q2 = sm.q[row0 + 4 * m + 2], q3 = sm.q[row0 + 4 * m + 3];
-        sfor<G>([&](auto gg) {
-          constexpr int g = CI(gg);
-          float s = q0 * S[4 * m][g];
-          s = __builtin_fmaf(q1, S[4 * m + 1][g], s);
-          s = __builtin_fmaf(q2, S[4 * m + 2][g], s);
-          s = __builtin_fmaf(q3, S[4 * m + 3][g], s);
-          tree_push<m>(lv[g], s);
-        });
-      }
     });
     if constexpr (kRead) {
       float o[G];
-      sfor<G>([&](auto gg) { o[CI(gg)] = lv[CI(gg)][4]; });
-      xwave_put<D, G>(sm, 1, w, lane, o);
+      row_dot<G>(S, [&](int r) { return rows.rb[r].q; }, o);
+      xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
-      xwave_sum<D, G>(sm, 1, lane, o);
-      store_out<D, G>(A, tile, w, lane, o);
+      xwave_sum<D>(sm, 1, lane, o);
+      store_out<D>(A, tile, w, lane, o);
       if constexpr (MODE == READ) {
-        put_stash<D, G, false>(A, tile, w, lane, trow, alpha, sm.bk[trow], e, u, vv);
+        put_stash<D, false>(A, tile, w, lane, row, alpha, sm.ra[row].bk, e, u, vv);
         return;
       }
     }
   }
   if constexpr (kWrite) {
-    sfor<R>([&](auto rr) {
-      constexpr int r = CI(rr);
-      float a;
-      if constexpr (G == 2) a = __builtin_fabsf(S[r][0]) + __builtin_fabsf(S[r][1]);
-      else a = __builtin_fabsf(S[r][0]);
-      sm.absT[w][r][lane] = a;
-    });
+    // ---- row factor from the row magnitudes
+    put_rowabs<D>(sm, S, lane);
     wave_lds_sync();
-    row_factor<D>(sm, w, lane, trow, den, om, false, rblk, fl);
+    row_factor<D>(sm, lane, row, den, om, false, rblk, fl);
     wave_lds_sync();
 
     // ---- phase 3: y = S / r_hat, first column factor c0 = max_i |y_ij| / qmax
     float mx[G];
-    sfor<G>([&](auto gg) { mx[CI(gg)] = 0.0f; });
-    sfor<R>([&](auto rr) {
-      constexpr int r = CI(rr);
-      const float ir = sm.ir[row0 + r];
-      sfor<G>([&](auto gg) {
-        constexpr int g = CI(gg);
-        S[r][g] = S[r][g] * ir;
-        mx[g] = __builtin_fmaxf(mx[g], __builtin_fabsf(S[r][g]));
-      });
-    });
-    if constexpr (D / 64 > 1) {
-      sfor<G>([&](auto gg) { sm.red[0][w][G * lane + CI(gg)] = mx[CI(gg)]; });
-      __syncthreads();
-      sfor<G>([&](auto gg) {
-        mx[CI(gg)] = __builtin_fmaxf(sm.red[0][0][G * lane + CI(gg)],
-                                     sm.red[0][1][G * lane + CI(gg)]);
-      });
-    }
+    scale_rows<G, false>(S, rows.rb, mx);
+    xwave_put<D>(sm, 0, w, lane, mx);
+    __syncthreads();
+    xwave_max<D>(sm, 0, lane, mx);
     float c0[G], ic0[G];
     sfor<G>([&](auto gg) {
-      c0[CI(gg)] = mx[CI(gg)] * IQ;  // = max_i(|y| * 1/qmax): rounding is monotone
+      c0[CI(gg)] = mx[CI(gg)] * IQ;
       ic0[CI(gg)] = rcp0(c0[CI(gg)]);
     });
 
-    // ---- phase 4: first quantization z0 and the omega-weighted least-squares sums
-    float ln[G][5], ls[G][5];
-    sfor<NQ>([&](auto mm) {
-      constexpr int m = CI(mm);
-      float W4[4];
-      sfor<4>([&](auto tt) { W4[CI(tt)] = sm.W[row0 + 4 * m + CI(tt)]; });
-      sfor<G>([&](auto gg) {
-        constexpr int g = CI(gg);
-        float sn = 0.0f, sq = 0.0f;
-        sfor<4>([&](auto tt) {
-          constexpr int r = 4 * m + CI(tt);
-          const float z0 = __builtin_rintf(S[r][g] * ic0[g]);  // |z0| <= qmax: no clamp
-          const float a = W4[CI(tt)] * z0;
-          if constexpr (CI(tt) == 0) {
-            sn = a * S[r][g];
-            sq = a * z0;
-          } else {
-            sn = __builtin_fmaf(a, S[r][g], sn);
-            sq = __builtin_fmaf(a, z0, sq);
-          }
-        });
-        tree_push<m>(ln[g], sn);
-        tree_push<m>(ls[g], sq);
-      });
-    });
-    float num[G], sq[G];
-    sfor<G>([&](auto gg) {
-      num[CI(gg)] = ln[CI(gg)][4];
-      sq[CI(gg)] = ls[CI(gg)][4];
-    });
-    if constexpr (D / 64 > 1) {
-      xwave_put<D, G>(sm, 0, w, lane, num);
-      xwave_put<D, G>(sm, 1, w, lane, sq);
-      __syncthreads();
-      xwave_sum<D, G>(sm, 0, lane, num);
-      xwave_sum<D, G>(sm, 1, lane, sq);
-    }
-    float ic[G];
-    sfor<G>([&](auto gg) {
-      constexpr int g = CI(gg);
-      const float c1 = sq[g] > 0.0f ? num[g] / sq[g] : c0[g];
-      const uint16_t ch = f2h(c1);
-      if (is_inf16(ch)) fl |= kFlagScaleOvf;
-      if (w == 0) cblk[G * lane + g] = ch;
-      ic[g] = rcp0(h2f(ch));
-    });
+    // ---- phase 4: first quantization and the least-squares column refit
+    float num[G], sq[G], ic[G];
+    ls_sums<G>(S, rows.rb, ic0, num, sq);
+    xwave_put<D>(sm, 1, w, lane, num);
+    xwave_put<D>(sm, 2, w, lane, sq);
+    __syncthreads();
+    xwave_sum<D>(sm, 1, lane, num);
+    xwave_sum<D>(sm, 2, lane, sq);
+    col_factor<G>(num, sq, c0, w, lane, cblk, ic, fl);
 
-    // ---- phase 5: final round-half-even requantization and packing
+    // ---- phase 5: final requantization and packing
     uint32_t acc = 0;
     auto store = [&](auto wi, uint32_t x) {
       __builtin_nontemporal_store(x, &words[(w * WPW + CI(wi)) * 64 + lane]);
     };
-    sfor<R * G>([&](auto kk2) {
-      constexpr int K = CI(kk2), r = K / G, g = K % G;
-      float t = __builtin_amdgcn_fmed3f(S[r][g] * ic[g], -QM, QM);
-      uint32_t f = __builtin_bit_cast(uint32_t, t + kMagic);
-      put_code<BITS, K>(acc, f, store);
+    sfor<R * G>([&](auto kk) {
+      constexpr int K = CI(kk), r = K / G, g = K % G;
+      put_code<BITS, K>(acc, __builtin_bit_cast(uint32_t, quant_off(S[r][g], ic[g], QM)), store);
     });
   }
   raise_flags(A, fl);
@@ -450,23 +565,22 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, Smem<D
 
 template <int D, int MODE>
 __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, int h, Smem<D>& sm) {
-  constexpr int G = D / 64, R = 64, NQ = R / 4;
+  using Gm = Geo<D>;
+  constexpr int G = Gm::G, R = Gm::R;
   constexpr bool kRead = MODE == FUSED || MODE == READ;
   constexpr bool kWrite = MODE != READ;
-  const int lane = threadIdx.x & 63, w = wave_id(), trow = threadIdx.x, row0 = w * R;
+  const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
   const long long tile = (long long)b * A.P.H + h;
   uint8_t* seg = A.pool + (long long)b * A.P.bpr + A.P.head_off[h];
   uint16_t* hblk = reinterpret_cast<uint16_t*>(seg);
+  const Rows<D> rows(sm);
   unsigned fl = 0;
   float S[R][G];
   float e[G], u[G], vv[G];
-  float alpha = 0.0f, beta = 0.0f;
+  float alpha = 0.0f;
 
   if constexpr (MODE == ENCODE) {
-    const float* src = A.S_in + tile * D * D;
-    sfor<R>([&](auto rr) {
-      sfor<G>([&](auto gg) { S[CI(rr)][CI(gg)] = src[(row0 + CI(rr)) * D + G * lane + CI(gg)]; });
-    });
+    load_state<D>(A, tile, row0, lane, S);
   } else {
     sfor<R>([&](auto rr) {
       sfor<G>([&](auto gg) {
@@ -474,95 +588,47 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, int h, Smem
       });
     });
   }
-  if constexpr (kRead) {
-    alpha = A.alpha[tile];
-    beta = A.beta[tile];
-    const float kk = A.k[tile * D + trow];
-    sm.k[trow] = kk;
-    sm.bk[trow] = beta * kk;
-    sm.q[trow] = A.q[tile * D + trow];
-    sfor<G>([&](auto gg) { vv[CI(gg)] = A.v[tile * D + G * lane + CI(gg)]; });
-  }
-  if constexpr (MODE == WRITE) {
-    const float* st = A.stash + tile * 4 * D;
-    alpha = st[0];
-    sm.bk[trow] = st[D + trow];
-    sfor<G>([&](auto gg) { e[CI(gg)] = st[2 * D + G * lane + CI(gg)]; });
-  }
+  load_inputs<D, MODE, false>(A, sm, tile, lane, row, nullptr, alpha, vv, e, u);
   wave_lds_sync();
-  if constexpr (kRead) {
-    float lv[G][5];
-    sfor<NQ>([&](auto mm) {
-      constexpr int m = CI(mm);
-      const float k0 = sm.k[row0 + 4 * m], k1 = sm.k[row0 + 4 * m + 1];
-      const float k2 = sm.k[row0 + 4 * m + 2], k3 = sm.k[row0 + 4 * m + 3];
-      sfor<G>([&](auto gg) {
-        constexpr int g = CI(gg);
-        float s = k0 * S[4 * m][g];
-        s = __builtin_fmaf(k1, S[4 * m + 1][g], s);
-        s = __builtin_fmaf(k2, S[4 * m + 2][g], s);
-        s = __builtin_fmaf(k3, S[4 * m + 3][g], s);
-        tree_push<m>(lv[g], s);
-      });
-    });
-    sfor<G>([&](auto gg) { u[CI(gg)] = lv[CI(gg)][4]; });
-    xwave_put<D, G>(sm, 0, w, lane, u);
-    __syncthreads();
-    xwave_sum<D, G>(sm, 0, lane, u);
-    sfor<G>([&](auto gg) { e[CI(gg)] = __builtin_fmaf(-alpha, u[CI(gg)], vv[CI(gg)]); });
-  }
   if constexpr (MODE != ENCODE) {
-    float lv[G][5];
-    sfor<NQ>([&](auto mm) {
-      constexpr int m = CI(mm);
-      sfor<4>([&](auto tt) {
-        constexpr int r = 4 * m + CI(tt);
-        const float bk = sm.bk[row0 + r];
-        sfor<G>([&](auto gg) {
-          S[r][CI(gg)] = __builtin_fmaf(alpha, S[r][CI(gg)], bk * e[CI(gg)]);
-        });
+    if constexpr (kRead) {
+      row_dot<G>(S, [&](int r) { return rows.ra[r].k; }, u);
+      xwave_put<D>(sm, 0, w, lane, u);
+      __syncthreads();
+      xwave_sum<D>(sm, 0, lane, u);
+      sfor<G>([&](auto gg) { e[CI(gg)] = __builtin_fmaf(-alpha, u[CI(gg)], vv[CI(gg)]); });
+    }
+    sfor<R>([&](auto rr) {
+      constexpr int r = CI(rr);
+      const float bk = rows.ra[r].bk;
+      sfor<G>([&](auto gg) {
+        S[r][CI(gg)] = __builtin_fmaf(alpha, S[r][CI(gg)], bk * e[CI(gg)]);
       });
-      if constexpr (kRead) {
-        const float q0 = sm.q[row0 + 4 * m], q1 = sm.q[row0 + 4 * m + 1];
-        const float q2 = sm.q[row0 + 4 * m + 2], q3 = sm.q[row0 + 4 * m + 3];
-        sfor<G>([&](auto gg) {
-          constexpr int g = CI(gg);
-          float s = q0 * S[4 * m][g];
-          s = __builtin_fmaf(q1, S[4 * m + 1][g], s);
-          s = __builtin_fmaf(q2, S[4 * m + 2][g], s);
-          s = __builtin_fmaf(q3, S[4 * m + 3][g], s);
-          tree_push<m>(lv[g], s);
-        });
-      }
     });
     if constexpr (kRead) {
       float o[G];
-      sfor<G>([&](auto gg) { o[CI(gg)] = lv[CI(gg)][4]; });
-      xwave_put<D, G>(sm, 1, w, lane, o);
+      row_dot<G>(S, [&](int r) { return rows.rb[r].q; }, o);
+      xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
-      xwave_sum<D, G>(sm, 1, lane, o);
-      store_out<D, G>(A, tile, w, lane, o);
+      xwave_sum<D>(sm, 1, lane, o);
+      store_out<D>(A, tile, w, lane, o);
       if constexpr (MODE == READ) {
-        put_stash<D, G, false>(A, tile, w, lane, trow, alpha, sm.bk[trow], e, u, vv);
+        put_stash<D, false>(A, tile, w, lane, row, alpha, sm.ra[row].bk, e, u, vv);
         return;
       }
     }
   }
   if constexpr (kWrite) {
+    put_rowabs<D>(sm, S, lane);
     sfor<R>([&](auto rr) {
-      constexpr int r = CI(rr);
-      float a;
-      if constexpr (G == 2) a = __builtin_fabsf(S[r][0]) + __builtin_fabsf(S[r][1]);
-      else a = __builtin_fabsf(S[r][0]);
-      sm.absT[w][r][lane] = a;
       sfor<G>([&](auto gg) {
-        const uint16_t hv = f2h(S[r][CI(gg)]);
+        const uint16_t hv = f2h(S[CI(rr)][CI(gg)]);
         if (is_inf16(hv)) fl |= kFlagPivotOvf;
-        hblk[(row0 + r) * D + G * lane + CI(gg)] = hv;
+        hblk[(row0 + CI(rr)) * D + G * lane + CI(gg)] = hv;
       });
     });
     wave_lds_sync();
-    row_factor<D>(sm, w, lane, trow, 1.0f, 0.0f, true, nullptr, fl);
+    row_factor<D>(sm, lane, row, 1.0f, 0.0f, true, nullptr, fl);
   }
   raise_flags(A, fl);
 }
@@ -574,10 +640,12 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, int h, Smem
 
 template <int D, int MODE>
 __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D>& sm) {
-  constexpr int G = D / 64, R = 64, NQ = R / 4, NT = D;
+  using Gm = Geo<D>;
+  constexpr int G = Gm::G, R = Gm::R, NT = Gm::NT;
   constexpr bool kRead = MODE == FUSED || MODE == READ;
   constexpr bool kWrite = MODE != READ;
-  const int lane = threadIdx.x & 63, w = wave_id(), trow = threadIdx.x, row0 = w * R;
+  const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
+  const int tid = threadIdx.x;
   const long long tile = (long long)b * A.P.H + h;
   uint8_t* seg = A.pool + (long long)b * A.P.bpr + A.P.head_off[h];
   uint32_t* words = reinterpret_cast<uint32_t*>(seg);
@@ -588,69 +656,51 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
   const int* bitsv = A.P.bits + h * D;
   const int* posv = A.P.rowpos + h * D;
   const int* pidv = A.P.pividx + h * D;
-  const int prow = h * D + trow;
+  const Rows<D> rows(sm);
   unsigned fl = 0;
   float S[R][G];
-  float u[G], vv[G], cc[G];
-  float beta = 0.0f, den = 1.0f, om = 0.0f;
+  float e[G], u[G], vv[G], cc[G];
+  float alpha = 0.0f;
 
   // ---- phase 0: stage the code block in LDS (coalesced 16-byte copies), per-row inputs
   if constexpr (MODE != ENCODE) {
-    const int n4 = nwords * 16;  // uint4 count: nwords * 64 lanes / 4
+    const int n4 = nwords * 16;  // 16-byte units: nwords * 64 lanes * 4 bytes / 16
     const u32x4* g4 = reinterpret_cast<const u32x4*>(words);
     u32x4* l4 = reinterpret_cast<u32x4*>(sm.code);
-    for (int x = trow; x < n4; x += NT) l4[x] = __builtin_nontemporal_load(&g4[x]);
-    if (trow < 16) l4[n4 + trow] = u32x4{0u, 0u, 0u, 0u};  // window over the last word
+    for (int x = tid; x < n4; x += NT) l4[x] = __builtin_nontemporal_load(&g4[x]);
+    if (tid < 16) l4[n4 + tid] = u32x4{0u, 0u, 0u, 0u};  // window over the last word
     sfor<G>([&](auto gg) { cc[CI(gg)] = h2f(cblk[G * lane + CI(gg)]); });
-    sm.r[trow] = h2f(rblk[trow]);
   }
-  if constexpr (kRead) {
-    beta = A.beta[tile];
-    const float kk = A.k[tile * D + trow];
-    const float ar = A.alpha[tile * D + trow];
-    sm.k[trow] = kk;
-    sm.bk[trow] = beta * kk;
-    sm.a[trow] = ar;
-    sm.q[trow] = A.q[tile * D + trow];
-    sfor<G>([&](auto gg) { vv[CI(gg)] = A.v[tile * D + G * lane + CI(gg)]; });
-  }
-  if constexpr (MODE == WRITE) {
-    const float* st = A.stash + tile * 4 * D;
-    sm.a[trow] = st[trow];
-    sm.bk[trow] = st[D + trow];
-    sfor<G>([&](auto gg) {
-      u[CI(gg)] = st[2 * D + G * lane + CI(gg)];
-      vv[CI(gg)] = st[3 * D + G * lane + CI(gg)];
-    });
-  }
+  load_inputs<D, MODE, true>(A, sm, tile, lane, row, MODE != ENCODE ? rblk : nullptr, alpha, vv,
+                             e, u);
+  float den = 1.0f, om = 0.0f;
   if constexpr (kWrite) {
-    den = A.P.den[prow];
-    om = A.P.omega[prow];
-    sm.iq[trow] = A.P.iq[prow];
-    sm.qm[trow] = A.P.qmax[prow];
+    den = A.P.den[h * D + row];
+    om = A.P.omega[h * D + row];
+    if (lane < 32) {
+      sm.rb[row].iq = A.P.iq[h * D + row];
+      sm.qm[row] = A.P.qmax[h * D + row];
+    }
   }
   __syncthreads();
 
   // ---- phase 1: dequantize, u
   if constexpr (MODE == ENCODE) {
-    const float* src = A.S_in + tile * D * D;
-    sfor<R>([&](auto rr) {
-      sfor<G>([&](auto gg) { S[CI(rr)][CI(gg)] = src[(row0 + CI(rr)) * D + G * lane + CI(gg)]; });
-    });
+    load_state<D>(A, tile, row0, lane, S);
   } else {
     sfor<R>([&](auto rr) {
       constexpr int r = CI(rr);
-      const int row = row0 + r;
-      const int pv = __builtin_amdgcn_readfirstlane(pidv[row]);
+      const int rw = row0 + r;
+      const int pv = __builtin_amdgcn_readfirstlane(pidv[rw]);
       if (pv >= 0) {
         sfor<G>([&](auto gg) { S[r][CI(gg)] = h2f(pblk[pv * D + G * lane + CI(gg)]); });
       } else {
-        const int bw = __builtin_amdgcn_readfirstlane(bitsv[row]);
-        const int p = __builtin_amdgcn_readfirstlane(posv[row]);
+        const int bw = __builtin_amdgcn_readfirstlane(bitsv[rw]);
+        const int p = __builtin_amdgcn_readfirstlane(posv[rw]);
         const uint32_t lo = sm.code[(p >> 5) * 64 + lane];
         const uint32_t hi = sm.code[((p >> 5) + 1) * 64 + lane];
         const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, p & 31);
-        const float rh = sm.r[row];
+        const float rh = rows.ra[r].r;
         sfor<G>([&](auto gg) {
           constexpr int g = CI(gg);
           const int z = __builtin_amdgcn_sbfe((int)x, g * bw, bw);
@@ -659,92 +709,53 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
       }
     });
     if constexpr (kRead) {
-      float lv[G][5];
-      sfor<NQ>([&](auto mm) {
-        constexpr int m = CI(mm);
-        const float k0 = sm.k[row0 + 4 * m], k1 = sm.k[row0 + 4 * m + 1];
-        const float k2 = sm.k[row0 + 4 * m + 2], k3 = sm.k[row0 + 4 * m + 3];
-        sfor<G>([&](auto gg) {
-          constexpr int g = CI(gg);
-          float s = k0 * S[4 * m][g];
-          s = __builtin_fmaf(k1, S[4 * m + 1][g], s);
-          s = __builtin_fmaf(k2, S[4 * m + 2][g], s);
-          s = __builtin_fmaf(k3, S[4 * m + 3][g], s);
-          tree_push<m>(lv[g], s);
-        });
-      });
-      sfor<G>([&](auto gg) { u[CI(gg)] = lv[CI(gg)][4]; });
-      xwave_put<D, G>(sm, 0, w, lane, u);
+      row_dot<G>(S, [&](int r) { return rows.ra[r].k; }, u);
+      xwave_put<D>(sm, 0, w, lane, u);
     }
   }
   __syncthreads();  // code block reads done (LDS reused below), cross-wave u staged
-  if constexpr (kRead) xwave_sum<D, G>(sm, 0, lane, u);
+  if constexpr (kRead) xwave_sum<D>(sm, 0, lane, u);
 
-  // ---- phase 2: update, readout, row magnitudes
+  // ---- phase 2: update, readout
   if constexpr (MODE != ENCODE) {
-    float lv[G][5];
-    sfor<NQ>([&](auto mm) {
-      constexpr int m = CI(mm);
-      sfor<4>([&](auto tt) {
-        constexpr int r = 4 * m + CI(tt);
-        const float ar = sm.a[row0 + r], bk = sm.bk[row0 + r];
-        sfor<G>([&](auto gg) {
-          constexpr int g = CI(gg);
-          const float ev = __builtin_fmaf(-ar, u[g], vv[g]);
-          S[r][g] = __builtin_fmaf(ar, S[r][g], bk * ev);
-        });
+    sfor<R>([&](auto rr) {
+      constexpr int r = CI(rr);
+      const float ar = rows.ra[r].a, bk = rows.ra[r].bk;
+      sfor<G>([&](auto gg) {
+        constexpr int g = CI(gg);
+        const float ev = __builtin_fmaf(-ar, u[g], vv[g]);
+        S[r][g] = __builtin_fmaf(ar, S[r][g], bk * ev);
       });
-      if constexpr (kRead) {
-        const float q0 = sm.q[row0 + 4 * m], q1 = sm.q[row0 + 4 * m + 1];
-        const float q2 = sm.q[row0 + 4 * m + 2], q3 = sm.q[row0 + 4 * m + 3];
-        sfor<G>([&](auto gg) {
-          constexpr int g = CI(gg);
-          float s = q0 * S[4 * m][g];
-          s = __builtin_fmaf(q1, S[4 * m + 1][g], s);
-          s = __builtin_fmaf(q2, S[4 * m + 2][g], s);
-          s = __builtin_fmaf(q3, S[4 * m + 3][g], s);
-          tree_push<m>(lv[g], s);
-        });
-      }
     });
     if constexpr (kRead) {
       float o[G];
-      sfor<G>([&](auto gg) { o[CI(gg)] = lv[CI(gg)][4]; });
-      xwave_put<D, G>(sm, 1, w, lane, o);
+      row_dot<G>(S, [&](int r) { return rows.rb[r].q; }, o);
+      xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
-      xwave_sum<D, G>(sm, 1, lane, o);
-      store_out<D, G>(A, tile, w, lane, o);
+      xwave_sum<D>(sm, 1, lane, o);
+      store_out<D>(A, tile, w, lane, o);
       if constexpr (MODE == READ) {
-        put_stash<D, G, true>(A, tile, w, lane, trow, sm.a[trow], sm.bk[trow], nullptr, u, vv);
+        put_stash<D, true>(A, tile, w, lane, row, sm.ra[row].a, sm.ra[row].bk, nullptr, u, vv);
         return;
       }
     }
   }
   if constexpr (kWrite) {
-    sfor<R>([&](auto rr) {
-      constexpr int r = CI(rr);
-      float a;
-      if constexpr (G == 2) a = __builtin_fabsf(S[r][0]) + __builtin_fabsf(S[r][1]);
-      else a = __builtin_fabsf(S[r][0]);
-      sm.absT[w][r][lane] = a;
-    });
+    put_rowabs<D>(sm, S, lane);
     wave_lds_sync();
-    const bool piv = A.P.pividx[prow] >= 0;
-    row_factor<D>(sm, w, lane, trow, den, om, piv, rblk, fl);
+    const bool piv = A.P.pividx[h * D + row] >= 0;
+    row_factor<D>(sm, lane, row, den, om, piv, rblk, fl);
     __syncthreads();  // absT dead for every wave: the code staging area is zeroed for packing
     {
       const int n4 = nwords * 16;
       u32x4* l4 = reinterpret_cast<u32x4*>(sm.code);
-      for (int x = trow; x < n4; x += NT) l4[x] = u32x4{0u, 0u, 0u, 0u};
+      for (int x = tid; x < n4; x += NT) l4[x] = u32x4{0u, 0u, 0u, 0u};
     }
 
-    // ---- phase 3: y, c0 = max_i |y_ij| / qmax_i ; pivot rows: store binary16
-    float mx[G];
-    sfor<G>([&](auto gg) { mx[CI(gg)] = 0.0f; });
+    // ---- phase 3: pivot rows stored as binary16; y and c0 = max_i |y_ij| / qmax_i
     sfor<R>([&](auto rr) {
       constexpr int r = CI(rr);
-      const int row = row0 + r;
-      const int pv = __builtin_amdgcn_readfirstlane(pidv[row]);
+      const int pv = __builtin_amdgcn_readfirstlane(pidv[row0 + r]);
       if (pv >= 0) {
         sfor<G>([&](auto gg) {
           const uint16_t hv = f2h(S[r][CI(gg)]);
@@ -752,23 +763,12 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
           pblk[pv * D + G * lane + CI(gg)] = hv;
         });
       }
-      const float ir = sm.ir[row], iq = sm.iq[row];
-      sfor<G>([&](auto gg) {
-        constexpr int g = CI(gg);
-        S[r][g] = S[r][g] * ir;
-        mx[g] = __builtin_fmaxf(mx[g], __builtin_fabsf(S[r][g]) * iq);
-      });
     });
-    if constexpr (D / 64 > 1) {
-      sfor<G>([&](auto gg) { sm.red[0][w][G * lane + CI(gg)] = mx[CI(gg)]; });
-    }
+    float mx[G];
+    scale_rows<G, true>(S, rows.rb, mx);
+    xwave_put<D>(sm, 0, w, lane, mx);
     __syncthreads();  // also orders the zeroing above before the packing below
-    if constexpr (D / 64 > 1) {
-      sfor<G>([&](auto gg) {
-        mx[CI(gg)] = __builtin_fmaxf(sm.red[0][0][G * lane + CI(gg)],
-                                     sm.red[0][1][G * lane + CI(gg)]);
-      });
-    }
+    xwave_max<D>(sm, 0, lane, mx);
     float c0[G], ic0[G];
     sfor<G>([&](auto gg) {
       c0[CI(gg)] = mx[CI(gg)];
@@ -776,51 +776,14 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
     });
 
     // ---- phase 4: z0 and least-squares sums
-    float ln[G][5], ls[G][5];
-    sfor<NQ>([&](auto mm) {
-      constexpr int m = CI(mm);
-      float W4[4];
-      sfor<4>([&](auto tt) { W4[CI(tt)] = sm.W[row0 + 4 * m + CI(tt)]; });
-      sfor<G>([&](auto gg) {
-        constexpr int g = CI(gg);
-        float sn = 0.0f, sq = 0.0f;
-        sfor<4>([&](auto tt) {
-          constexpr int r = 4 * m + CI(tt);
-          const float z0 = __builtin_rintf(S[r][g] * ic0[g]);
-          const float a = W4[CI(tt)] * z0;
-          if constexpr (CI(tt) == 0) {
-            sn = a * S[r][g];
-            sq = a * z0;
-          } else {
-            sn = __builtin_fmaf(a, S[r][g], sn);
-            sq = __builtin_fmaf(a, z0, sq);
-          }
-        });
-        tree_push<m>(ln[g], sn);
-        tree_push<m>(ls[g], sq);
-      });
-    });
-    float num[G], sq[G];
-    sfor<G>([&](auto gg) {
-      num[CI(gg)] = ln[CI(gg)][4];
-      sq[CI(gg)] = ls[CI(gg)][4];
-    });
-    if constexpr (D / 64 > 1) {
-      xwave_put<D, G>(sm, 0, w, lane, num);
-      xwave_put<D, G>(sm, 1, w, lane, sq);
-      __syncthreads();
-      xwave_sum<D, G>(sm, 0, lane, num);
-      xwave_sum<D, G>(sm, 1, lane, sq);
-    }
-    float ic[G];
-    sfor<G>([&](auto gg) {
-      constexpr int g = CI(gg);
-      const float c1 = sq[g] > 0.0f ? num[g] / sq[g] : c0[g];
-      const uint16_t ch = f2h(c1);
-      if (is_inf16(ch)) fl |= kFlagScaleOvf;
-      if (w == 0) cblk[G * lane + g] = ch;
-      ic[g] = rcp0(h2f(ch));
-    });
+    float num[G], sq[G], ic[G];
+    ls_sums<G>(S, rows.rb, ic0, num, sq);
+    xwave_put<D>(sm, 1, w, lane, num);
+    xwave_put<D>(sm, 2, w, lane, sq);
+    __syncthreads();
+    xwave_sum<D>(sm, 1, lane, num);
+    xwave_sum<D>(sm, 2, lane, sq);
+    col_factor<G>(num, sq, c0, w, lane, cblk, ic, fl);
 
     // ---- phase 5: requantize and pack into the LDS stream (uniform positions), then copy out
     {
@@ -834,21 +797,20 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
       };
       sfor<R>([&](auto rr) {
         constexpr int r = CI(rr);
-        const int row = row0 + r;
-        const int bw = __builtin_amdgcn_readfirstlane(bitsv[row]);
-        if (__builtin_amdgcn_readfirstlane(pidv[row]) < 0) {
-          const int p = __builtin_amdgcn_readfirstlane(posv[row]);
-          const float qm = sm.qm[row];
+        const int rw = row0 + r;
+        const int bw = __builtin_amdgcn_readfirstlane(bitsv[rw]);
+        if (__builtin_amdgcn_readfirstlane(pidv[rw]) < 0) {
+          const int p = __builtin_amdgcn_readfirstlane(posv[rw]);
+          const float qm = rows.qm[r];
           const uint32_t mask = (1u << bw) - 1u;
           uint32_t wv = 0;
           sfor<G>([&](auto gg) {
             constexpr int g = CI(gg);
-            const float t = __builtin_amdgcn_fmed3f(S[r][g] * ic[g], -qm, qm);
-            const uint32_t f = __builtin_bit_cast(uint32_t, t + kMagic) & mask;
+            const uint32_t f = __builtin_bit_cast(uint32_t, quant_off(S[r][g], ic[g], qm)) & mask;
             wv |= f << (g * bw);
           });
           if (cw < 0) cw = p >> 5;
-          while ((p >> 5) > cw) {  // uniform: move to the word holding this row's first bit
+          while ((p >> 5) > cw) {  // uniform: advance to the word holding this row's first bit
             flush(first);
             first = false;
             acc >>= 32;
@@ -869,7 +831,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
       const int n4 = nwords * 16;
       u32x4* g4 = reinterpret_cast<u32x4*>(words);
       const u32x4* l4 = reinterpret_cast<const u32x4*>(sm.code);
-      for (int x = trow; x < n4; x += NT) __builtin_nontemporal_store(l4[x], &g4[x]);
+      for (int x = tid; x < n4; x += NT) __builtin_nontemporal_store(l4[x], &g4[x]);
     }
   }
   raise_flags(A, fl);
@@ -880,7 +842,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
 // ---------------------------------------------------------------------------------------------
 
 template <int D, int MODE>
-__global__ __launch_bounds__(D) void k_gdn(StepArgs A) {
+__global__ __launch_bounds__(Geo<D>::NT) void k_gdn(StepArgs A) {
   __shared__ Smem<D> sm;
   const int tile = blockIdx.x;
   const int b = tile / A.P.H, h = tile - b * A.P.H;
@@ -894,7 +856,7 @@ __global__ __launch_bounds__(D) void k_gdn(StepArgs A) {
 }
 
 template <int D, int MODE>
-__global__ __launch_bounds__(D) void k_kda(StepArgs A) {
+__global__ __launch_bounds__(Geo<D>::NT) void k_kda(StepArgs A) {
   __shared__ Smem<D> sm;
   const int tile = blockIdx.x;
   const int b = tile / A.P.H, h = tile - b * A.P.H;
@@ -945,7 +907,7 @@ __global__ __launch_bounds__(D) void k_unpack(DevPlan P, const uint8_t* pool, fl
 
 template <int D, int KIND>
 hipError_t launch_kind(Mode mode, const StepArgs& a, hipStream_t s) {
-  const dim3 grid(a.B * a.P.H), block(D);
+  const dim3 grid(a.B * a.P.H), block(Geo<D>::NT);
   switch (mode) {
     case FUSED:
       if constexpr (KIND == 0) hipLaunchKernelGGL((k_gdn<D, FUSED>), grid, block, 0, s, a);

@@ -251,3 +251,93 @@ def run_layer(w, layer, bits, piv, om, steps, tiles=None, mode=0, S0=None, check
                 seg_o[t] = gs.copy()  # continue from the GPU's state (teacher forcing)
         tr.steps += 1
     return tr, plan, pool
+
+
+def sample_tiles(w, per_head=1, extra=0, seed=0):
+    """Tiles to check: per_head requests for every head (request index spread over the batch),
+    plus `extra` random tiles."""
+    g = np.random.default_rng(seed)
+    tiles = []
+    for h in range(w.H):
+        for j in range(per_head):
+            b = (h * 7 + j * 13) % w.B
+            tiles.append(b * w.H + h)
+    tiles += list(g.choice(w.B * w.H, extra, replace=False))
+    return sorted(set(int(t) for t in tiles))
+
+
+def run_layers_split(w, plans_np, steps, tiles_per_layer, fused_check_layer=0):
+    """Multi-layer workload, layers stepped back to back each decode step with the refit and
+    writeback on the library's side stream (split mode).  The oracle checks the sampled tiles
+    of every layer after every step; one layer also runs a fused plan side by side on the same
+    inputs and must match the split result bit for bit."""
+    import torch
+    from quantized_delta_rule_amd import stepq
+
+    d, H, B = w.d, w.H, w.B
+    dev = torch.device("cuda:0")
+    bits, piv, om = plans_np
+    plans, pools, heads, segs_o, tiles = [], [], [], [], []
+    for l in range(w.layers):
+        log(f"[parity] layer {l}: warm-up and encode")
+        plan = stepq.Plan(stepq.GDN, bits[l], piv[l], om[l], mode=stepq.SPLIT, max_batch=B)
+        S0 = warm_state(w, l)
+        pool = plan.alloc_pool(B)
+        plan.encode(torch.from_numpy(S0).to(dev), pool, B)
+        hl = [oracle.Head(bits[l, h], piv[l, h], om[l, h]) for h in range(H)]
+        tl = tiles_per_layer(l)
+        so = {t: hl[t % H].encode(S0[t]) for t in tl}
+        if l == fused_check_layer:
+            fplan = stepq.Plan(stepq.GDN, bits[l], piv[l], om[l])
+            fpool = fplan.alloc_pool(B)
+            fplan.encode(torch.from_numpy(S0).to(dev), fpool, B)
+        del S0
+        plans.append(plan)
+        pools.append(pool)
+        heads.append(hl)
+        segs_o.append(so)
+        tiles.append(tl)
+    torch.cuda.synchronize()
+    tr = Tracker()
+    for s in range(steps):
+        xs = [synth.step_inputs(w, l, s, "decode") for l in range(w.layers)]
+        outs = []
+        for l in range(w.layers):
+            g = {k_: torch.from_numpy(v_).to(dev) for k_, v_ in xs[l].items()}
+            out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+            plans[l].step(pools[l], B, g["q"], g["k"], g["v"], g["alpha"], g["beta"], out)
+            outs.append(out)
+            if l == fused_check_layer:
+                fout = torch.empty_like(out)
+                fplan.step(fpool, B, g["q"], g["k"], g["v"], g["alpha"], g["beta"], fout)
+        for p in plans:
+            p.sync()
+        torch.cuda.synchronize()
+        fl = fused_check_layer
+        if not torch.equal(pools[fl], fpool) or not torch.equal(outs[fl], fout):
+            raise Mismatch(f"step {s}: split and fused results differ on layer {fl}")
+        for l in range(w.layers):
+            host = pools[l].cpu().numpy()
+            outh = outs[l].cpu().numpy()
+            a_rows = synth.alpha_rows(w, xs[l]["alpha"])
+            bpr = plans[l].bytes_per_request
+            for t in tiles[l]:
+                b, h = divmod(t, H)
+                x = xs[l]
+                o, S_upd, pre, _ = heads[l][h].step(segs_o[l][t], x["q"][b, h], x["k"][b, h],
+                                                     x["v"][b, h], a_rows[b, h], x["beta"][b, h],
+                                                     want_state=True)
+                err = rel_l2(outh[b, h], o)
+                tr.worst_readout = max(tr.worst_readout, err)
+                if err > READOUT_TOL:
+                    raise Mismatch(f"step {s} layer {l} tile {t}: readout rel L2 {err:.3e}")
+                off, n = plans[l].head_segment(h)
+                gs = host[b * bpr + off: b * bpr + off + n]
+                nb = compare_segment(heads[l][h], gs, segs_o[l][t], pre,
+                                     f"step {s} layer {l} tile {t}")
+                if nb:
+                    tr.boundary += nb
+                    segs_o[l][t] = gs.copy()
+        tr.steps += 1
+        log(f"[parity] step {s} ok (worst readout {tr.worst_readout:.2e}, boundary {tr.boundary})")
+    return tr, plans
