@@ -16,7 +16,9 @@
  *     fit over value columns with r fixed; z are low-bit integers stored per the offline map.
  *   - Method 4, "the execution path of each decode step": reconstruct from codes, scales and FP16
  *     pivots; retention + delta update + readout on the float tile; the output leaves before
- *     requantization; refit r and c; pack codes and scales with pivots kept in FP16.
+ *     requantization; refit r and c; pack codes and scales with pivots kept in FP16.  The row
+ *     factor of the reconstruction enters the update through the row coefficients k_i r_i and
+ *     a_i r_i (same product, one rounding fewer per entry than forming r_i c_j z_ij first).
  * The scale formulas (r_i = (mean_j|S_ij| + 1e-8)/(1 + omega_i/mean omega), c_j initialised to
  * max_i|S_ij/r_i|/qmax, one omega-weighted least-squares refit with z fixed, symmetric
  * round-half-even with qmax = 2^(b-1)-1) and the gate A_t = Diag(a)(I - beta k k^T) are the
@@ -371,24 +373,52 @@ done:
 /* the decode step (Method 4)                                                                 */
 /* ------------------------------------------------------------------------------------------ */
 
-/* One gated delta step on a decoded tile, in place on S (dk x dv):
+/* One gated delta step, in place, on a tile given as per-row factors f_i (the binary16 row
+   factor r_hat_i of a quantized row, 1 for a pivot row or an unquantized state) times a matrix X
+   (c_j z_ij, exact; or the pivot / fp32 values), so that the decoded state is f_i X_ij:
      u = S^T k;   S_ij <- a_i S_ij + (beta k_i) (v_j - a_i u_j);   out = S^T q
    which is S <- A S + beta k v^T with A = Diag(a)(I - beta k k^T) (GDN: every a_i = alpha).
-   Evaluation: e = fma(-a_i, u_j, v_j); S = fma(a_i, S, (beta*k_i) * e). */
-static void delta_update_readout(int dk, int dv, float* S, const float* q, const float* k,
-                                 const float* v, const float* a, float beta, float* out) {
+   The row factor enters through the row coefficients k_i f_i and a_i f_i:
+     u_j = dot_i(k_i f_i, X_ij);  e = fma(-a_i, u_j, v_j);  S_ij = fma(a_i f_i, X_ij, (beta k_i) e)
+   With a = 1 and beta = 0 this returns S_ij = f_i X_ij rounded once: the decoded state. */
+static void delta_update_readout(int dk, int dv, float* S, const float* f, const float* q,
+                                 const float* k, const float* v, const float* a, float beta,
+                                 float* out) {
   float* u = (float*)malloc(sizeof(float) * dv);
-  for (int j = 0; j < dv; j++) u[j] = dot_fixed(k, 1, S + j, dv, dk);
+  float* kf = (float*)malloc(sizeof(float) * dk);
+  for (int i = 0; i < dk; i++) kf[i] = k[i] * f[i];
+  for (int j = 0; j < dv; j++) u[j] = dot_fixed(kf, 1, S + j, dv, dk);
   for (int i = 0; i < dk; i++) {
-    float bk = beta * k[i];
+    float bk = beta * k[i], af = a[i] * f[i];
     for (int j = 0; j < dv; j++) {
       long e = (long)i * dv + j;
       float ev = fmaf(-a[i], u[j], v[j]);
-      S[e] = fmaf(a[i], S[e], bk * ev);
+      S[e] = fmaf(af, S[e], bk * ev);
     }
   }
   for (int j = 0; j < dv; j++) out[j] = dot_fixed(q, 1, S + j, dv, dk);
   free(u);
+  free(kf);
+}
+
+/* Splits a segment into per-row factors f (r_hat, or 1 on pivot rows) and X = c_j z_ij (exact)
+   or the pivot row's binary16 values.  Returns -1 on a corrupt code. */
+static int decode_factored(int dk, int dv, const int8_t* bits, const uint8_t* pivot,
+                           const uint8_t* seg, float* X, float* f) {
+  int8_t* z = (int8_t*)malloc((size_t)dk * dv);
+  float* Sh = (float*)malloc(sizeof(float) * dk * dv);
+  uint16_t* r16 = (uint16_t*)malloc(sizeof(uint16_t) * dk);
+  uint16_t* c16 = (uint16_t*)malloc(sizeof(uint16_t) * dv);
+  int rc = orc_unpack(dk, dv, bits, pivot, seg, Sh, r16, c16, z);
+  for (int i = 0; i < dk; i++) {
+    f[i] = pivot[i] ? 1.0f : orc_f16_to_f32(r16[i]);
+    for (int j = 0; j < dv; j++) {
+      long e = (long)i * dv + j;
+      X[e] = pivot[i] ? Sh[e] : orc_f16_to_f32(c16[j]) * (float)z[e];
+    }
+  }
+  free(z); free(Sh); free(r16); free(c16);
+  return rc;
 }
 
 /* Decode step of one (request, head) tile, in place on seg.  a has dk entries (all equal for
@@ -398,8 +428,10 @@ int orc_tile_step(int dk, int dv, const int8_t* bits, const uint8_t* pivot, cons
                   uint8_t* seg, const float* q, const float* k, const float* v, const float* a,
                   float beta, float* out, float* S_upd, double* pre, uint32_t* flags) {
   float* S = (float*)malloc(sizeof(float) * dk * dv);
-  int rc = orc_unpack(dk, dv, bits, pivot, seg, S, NULL, NULL, NULL);
-  delta_update_readout(dk, dv, S, q, k, v, a, beta, out);
+  float* f = (float*)malloc(sizeof(float) * dk);
+  int rc = decode_factored(dk, dv, bits, pivot, seg, S, f);
+  delta_update_readout(dk, dv, S, f, q, k, v, a, beta, out);
+  free(f);
   if (S_upd) memcpy(S_upd, S, sizeof(float) * dk * dv);
   orc_encode(dk, dv, bits, pivot, omega, S, seg, pre, flags);
   free(S);
@@ -409,7 +441,10 @@ int orc_tile_step(int dk, int dv, const int8_t* bits, const uint8_t* pivot, cons
 /* FP32-state mode: the same update and readout on an unquantized state (warm-up, drift). */
 void orc_fp32_step(int dk, int dv, float* S, const float* q, const float* k, const float* v,
                    const float* a, float beta, float* out) {
-  delta_update_readout(dk, dv, S, q, k, v, a, beta, out);
+  float* f = (float*)malloc(sizeof(float) * dk);
+  for (int i = 0; i < dk; i++) f[i] = 1.0f;
+  delta_update_readout(dk, dv, S, f, q, k, v, a, beta, out);
+  free(f);
 }
 
 /* ------------------------------------------------------------------------------------------ */
