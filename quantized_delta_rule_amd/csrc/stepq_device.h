@@ -20,8 +20,9 @@
 //   wave-uniform addresses (broadcast reads, no VALU work).
 //
 // Arithmetic matches a fixed binary32 evaluation order bit for bit:
-//   dequant  S_hat = r_i c_j z_ij rounded once (c_j z_ij is exact)
-//   update   e = fma(-a_i, u_j, v_j);  S = fma(a_i, S_hat, (beta k_i) e)
+//   dequant  X_ij = c_j z_ij (exact); the row factor r_i enters through the row coefficients
+//            k_i r_i and a_i r_i (pivot rows: X = the binary16 values, factor 1)
+//   update   u = dot_i(k_i r_i, X);  e = fma(-a_i, u_j, v_j);  S = fma(a_i r_i, X, (beta k_i) e)
 //   sums     aligned groups of 4 rows accumulated with fma first to last, the group sums then
 //            added as a pairwise tree; the row magnitude sum is a pairwise tree over columns
 //   codes    round-half-even of the exact product y * (1/c): fma(y, 1/c, 1.5*2^23) rounds the
@@ -108,34 +109,57 @@ struct Geo {
 };
 
 // Per-row records, read at wave-uniform addresses (broadcast reads).
-struct RowA { float r, k, a, bk; };   // decode, u, update
+struct RowA { float kr, ar, a, bk; };  // u (k r), update (a r, a, beta k)
 struct RowB { float q, ir, W, iq; };  // readout, row factor, least squares, column maximum
 
+template <int D, bool KDA>
+struct RowsKda {  // per-row 1/qmax and qmax of mixed-width tiles
+  float iq[D], qm[D];
+};
 template <int D>
+struct RowsKda<D, false> {};
+template <int D, bool KDA>
+struct CodeKda {  // code block staging of mixed-width tiles
+  uint32_t code[(2 * D * 8 / 32 + 1) * 64];
+};
+template <int D>
+struct CodeKda<D, false> {};
+
+// GDN tiles need 40 KB, so four workgroups fit in a CU's 160 KB: their per-row 1/qmax and qmax
+// are compile-time constants, and the column maxima pass through each wave's own (by then dead)
+// transpose section, so two cross-wave slots suffice.
+template <int D, bool KDA>
 struct Smem {
   static constexpr int NW = Geo<D>::NW;
+  static constexpr bool kKDA = KDA;
+  static constexpr int NSLOT = KDA ? 3 : 2;
   RowA ra[D];
-  RowB rb[D];
-  float qm[D];
-  float red[3][NW][D];
+  float q[D], ir[D], W[D];
+  [[no_unique_address]] RowsKda<D, KDA> kr;
+  float red[NSLOT][NW][D];
   union {
-    float absT[NW][32][65];                    // [wave][row][lane], +1 pad: conflict-free
-    uint32_t code[(2 * D * 8 / 32 + 1) * 64];  // mixed-width tiles: code block staging
+    float absT[NW][32][65];  // [wave][row][lane], +1 pad: conflict-free
+    CodeKda<D, KDA> kc;      // used only before and after the transpose
   };
 };
 
 // Wave-local views: the base index comes from threadIdx, so it stays in a VGPR and every
 // per-row read is one ds_read with an immediate offset.
-template <int D>
+template <typename SM>
 struct Rows {
   const RowA* ra;
-  const RowB* rb;
-  const float* qm;
-  __device__ __forceinline__ Rows(const Smem<D>& sm) {
+  const float *q, *ir, *W, *iq, *qm;
+  __device__ __forceinline__ Rows(const SM& sm) {
     const int base = (threadIdx.x >> 6) * 32;
     ra = sm.ra + base;
-    rb = sm.rb + base;
-    qm = sm.qm + base;
+    q = sm.q + base;
+    ir = sm.ir + base;
+    W = sm.W + base;
+    iq = qm = nullptr;
+    if constexpr (SM::kKDA) {
+      iq = sm.kr.iq + base;
+      qm = sm.kr.qm + base;
+    }
   }
 };
 
@@ -202,15 +226,14 @@ __device__ __forceinline__ void row_dot(const float (&S)[32][G], XF&& xr, float*
 }
 
 // Cross-wave combination of this lane's per-wave partials (red[slot][w][col]).
-template <int D>
-__device__ __forceinline__ void xwave_put(Smem<D>& sm, int slot, int w, int lane,
-                                          const float* x) {
+template <int D, typename SM>
+__device__ __forceinline__ void xwave_put(SM& sm, int slot, int w, int lane, const float* x) {
   constexpr int G = Geo<D>::G;
   sfor<G>([&](auto gg) { sm.red[slot][w][G * lane + CI(gg)] = x[CI(gg)]; });
 }
 // pairwise tree over the waves' partials (rows 0-31, 32-63, ...)
-template <int D>
-__device__ __forceinline__ void xwave_sum(Smem<D>& sm, int slot, int lane, float* x) {
+template <int D, typename SM>
+__device__ __forceinline__ void xwave_sum(SM& sm, int slot, int lane, float* x) {
   constexpr int G = Geo<D>::G, NW = Geo<D>::NW;
   sfor<G>([&](auto gg) {
     const int c = G * lane + CI(gg);
@@ -222,21 +245,33 @@ __device__ __forceinline__ void xwave_sum(Smem<D>& sm, int slot, int lane, float
     }
   });
 }
-template <int D>
-__device__ __forceinline__ void xwave_max(Smem<D>& sm, int slot, int lane, float* x) {
+// Column maxima across waves: GDN tiles stage them in each wave's own transpose section (dead
+// once that wave's row factors are done), KDA tiles in cross-wave slot 2.
+template <int D, typename SM>
+__device__ __forceinline__ float* max_slot(SM& sm, int w) {
+  if constexpr (SM::kKDA) return &sm.red[2][w][0];
+  else return &sm.absT[w][0][0];
+}
+template <int D, typename SM>
+__device__ __forceinline__ void xwave_max_put(SM& sm, int w, int lane, const float* x) {
+  constexpr int G = Geo<D>::G;
+  float* dst = max_slot<D>(sm, w);
+  sfor<G>([&](auto gg) { dst[G * lane + CI(gg)] = x[CI(gg)]; });
+}
+template <int D, typename SM>
+__device__ __forceinline__ void xwave_max(SM& sm, int lane, float* x) {
   constexpr int G = Geo<D>::G, NW = Geo<D>::NW;
   sfor<G>([&](auto gg) {
     const int c = G * lane + CI(gg);
-    float m = sm.red[slot][0][c];
-    sfor<NW - 1>([&](auto ww) { m = __builtin_fmaxf(m, sm.red[slot][CI(ww) + 1][c]); });
+    float m = max_slot<D>(sm, 0)[c];
+    sfor<NW - 1>([&](auto ww) { m = __builtin_fmaxf(m, max_slot<D>(sm, CI(ww) + 1)[c]); });
     x[CI(gg)] = m;
   });
 }
 
 // |S| partial sums of each row over this lane's columns, transposed through LDS.
-template <int D>
-__device__ __forceinline__ void put_rowabs(Smem<D>& sm, const float (&S)[32][Geo<D>::G],
-                                           int lane) {
+template <int D, typename SM>
+__device__ __forceinline__ void put_rowabs(SM& sm, const float (&S)[32][Geo<D>::G], int lane) {
   constexpr int G = Geo<D>::G;
   float* dst = &sm.absT[0][0][0] + (threadIdx.x >> 6) * (32 * 65) + lane;
   sfor<32>([&](auto rr) {
@@ -252,8 +287,8 @@ __device__ __forceinline__ void put_rowabs(Smem<D>& sm, const float (&S)[32][Geo
 // halves are added, and lane L < 32 writes r_hat to the pool (unless rblk is null) and
 // ir = 1/r_hat (0 if dead or pivot) and W = (omega r_hat) r_hat (0 likewise) into the row
 // record.
-template <int D>
-__device__ __forceinline__ void row_factor(Smem<D>& sm, int lane, int row, float den, float om,
+template <int D, typename SM>
+__device__ __forceinline__ void row_factor(SM& sm, int lane, int row, float den, float om,
                                            bool piv, uint16_t* rblk, unsigned& fl) {
   float lv[6];
   const float* src =
@@ -264,8 +299,8 @@ __device__ __forceinline__ void row_factor(Smem<D>& sm, int lane, int row, float
   if (!__builtin_isfinite(m)) fl |= kFlagNonfinite;
   if (lane >= 32) return;
   if (piv) {
-    sm.rb[row].ir = 0.0f;
-    sm.rb[row].W = 0.0f;
+    sm.ir[row] = 0.0f;
+    sm.W[row] = 0.0f;
     if (rblk) rblk[row] = 0;
     return;
   }
@@ -274,20 +309,20 @@ __device__ __forceinline__ void row_factor(Smem<D>& sm, int lane, int row, float
   if (is_inf16(rh)) fl |= kFlagScaleOvf;
   if (rblk) rblk[row] = rh;
   const float rf = h2f(rh);
-  sm.rb[row].ir = rcp0(rf);
-  sm.rb[row].W = (om * rf) * rf;
+  sm.ir[row] = rcp0(rf);
+  sm.W[row] = (om * rf) * rf;
 }
 
 // y = S * ir (in place) and the column maximum max_i |y| (GDN: one width, the 1/qmax factor
 // is applied after the maximum -- rounding is monotone) or max_i |y| / qmax_i (KDA).
-template <int G, bool KDA>
-__device__ __forceinline__ void scale_rows(float (&S)[32][G], const RowB* rb, float* mx) {
+template <int G, bool KDA, typename RW>
+__device__ __forceinline__ void scale_rows(float (&S)[32][G], const RW& rows, float* mx) {
   sfor<G>([&](auto gg) { mx[CI(gg)] = 0.0f; });
   sfor<32>([&](auto rr) {
     constexpr int r = CI(rr);
-    const float ir = rb[r].ir;
+    const float ir = rows.ir[r];
     float iq = 0.0f;
-    if constexpr (KDA) iq = rb[r].iq;
+    if constexpr (KDA) iq = rows.iq[r];
     sfor<G>([&](auto gg) {
       constexpr int g = CI(gg);
       S[r][g] = S[r][g] * ir;
@@ -299,14 +334,14 @@ __device__ __forceinline__ void scale_rows(float (&S)[32][G], const RowB* rb, fl
 
 // First quantization z0 = rne(y / c0) and the sums of the omega-weighted least-squares fit:
 // num = sum_i (W_i z0) y, sq = sum_i (W_i z0) z0, both as fma chains of four + pairwise tree.
-template <int G>
-__device__ __forceinline__ void ls_sums(const float (&S)[32][G], const RowB* rb, const float* ic0,
+template <int G, typename RW>
+__device__ __forceinline__ void ls_sums(const float (&S)[32][G], const RW& rows, const float* ic0,
                                         float* num, float* sq) {
   float ln[G][4], ls[G][4];
   sfor<8>([&](auto mm) {
     constexpr int m = CI(mm);
     float W4[4];
-    sfor<4>([&](auto tt) { W4[CI(tt)] = rb[4 * m + CI(tt)].W; });
+    sfor<4>([&](auto tt) { W4[CI(tt)] = rows.W[4 * m + CI(tt)]; });
     sfor<G>([&](auto gg) {
       constexpr int g = CI(gg);
       float sn = 0.0f, sqv = 0.0f;
@@ -391,8 +426,8 @@ __device__ __forceinline__ void load_state(const StepArgs& A, long long tile, in
 
 // Per-tile inputs of a step: row records (lanes 0..31 of each wave fill their wave's rows),
 // per-column v or the hand-over.  Returns alpha (GDN) and fills vv / e / u.
-template <int D, int MODE, bool KDA>
-__device__ __forceinline__ void load_inputs(const StepArgs& A, Smem<D>& sm, long long tile,
+template <int D, int MODE, bool KDA, typename SM>
+__device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long tile,
                                             int lane, int row, const uint16_t* rblk,
                                             float& alpha, float* vv, float* e, float* u) {
   constexpr int G = Geo<D>::G;
@@ -415,20 +450,23 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, Smem<D>& sm, long
   }
   if (lane < 32) {
     RowA ra{};
-    if (rblk) ra.r = h2f(rblk[row]);
+    // row factor: r_hat of a quantized row; 1 on pivot rows and FP16 pivot heads
+    float rf = 1.0f;
+    if (rblk && !(KDA && A.P.pividx[(tile % A.P.H) * D + row] >= 0)) rf = h2f(rblk[row]);
     if constexpr (kRead) {
       const float beta = A.beta[tile];
       const float kk = A.k[tile * D + row];
-      ra.k = kk;
+      ra.kr = kk * rf;
       ra.bk = beta * kk;
       ra.a = KDA ? A.alpha[tile * D + row] : alpha;
-      sm.rb[row].q = A.q[tile * D + row];
+      sm.q[row] = A.q[tile * D + row];
     }
     if constexpr (MODE == WRITE) {
       const float* st = A.stash + tile * 4 * D;
       ra.a = st[row];
       ra.bk = st[D + row];
     }
+    ra.ar = ra.a * rf;
     sm.ra[row] = ra;
   }
 }
@@ -437,8 +475,8 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, Smem<D>& sm, long
 // GDN: a whole head at one width
 // ---------------------------------------------------------------------------------------------
 
-template <int D, int MODE, int BITS>
-__device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, Smem<D>& sm) {
+template <int D, int MODE, int BITS, typename SM>
+__device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, SM& sm) {
   using Gm = Geo<D>;
   constexpr int G = Gm::G, R = Gm::R;
   constexpr int WPW = R * G * BITS / 32;  // code words per lane for one wave's rows
@@ -452,7 +490,7 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, Smem<D
   uint32_t* words = reinterpret_cast<uint32_t*>(seg);
   uint16_t* rblk = reinterpret_cast<uint16_t*>(seg + A.P.off_r[h]);
   uint16_t* cblk = reinterpret_cast<uint16_t*>(seg + A.P.off_c[h]);
-  const Rows<D> rows(sm);
+  const Rows<SM> rows(sm);
   unsigned fl = 0;
 
   float S[R][G];
@@ -482,14 +520,13 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, Smem<D
     // ---- phase 1: dequantize, and u = S_hat^T k
     sfor<R>([&](auto rr) {
       constexpr int r = CI(rr);
-      const float rh = rows.ra[r].r;
       sfor<G>([&](auto gg) {
         constexpr int g = CI(gg);
-        S[r][g] = rh * (cc[g] * (float)get_code<BITS, r * G + g>(wd));
+        S[r][g] = cc[g] * (float)get_code<BITS, r * G + g>(wd);
       });
     });
     if constexpr (kRead) {
-      row_dot<G>(S, [&](int r) { return rows.ra[r].k; }, u);
+      row_dot<G>(S, [&](int r) { return rows.ra[r].kr; }, u);
       xwave_put<D>(sm, 0, w, lane, u);
       __syncthreads();
       xwave_sum<D>(sm, 0, lane, u);
@@ -499,14 +536,14 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, Smem<D
     // ---- phase 2: gated delta update and readout
     sfor<R>([&](auto rr) {
       constexpr int r = CI(rr);
-      const float bk = rows.ra[r].bk;
+      const float ar = rows.ra[r].ar, bk = rows.ra[r].bk;
       sfor<G>([&](auto gg) {
-        S[r][CI(gg)] = __builtin_fmaf(alpha, S[r][CI(gg)], bk * e[CI(gg)]);
+        S[r][CI(gg)] = __builtin_fmaf(ar, S[r][CI(gg)], bk * e[CI(gg)]);
       });
     });
     if constexpr (kRead) {
       float o[G];
-      row_dot<G>(S, [&](int r) { return rows.rb[r].q; }, o);
+      row_dot<G>(S, [&](int r) { return rows.q[r]; }, o);
       xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
       xwave_sum<D>(sm, 1, lane, o);
@@ -526,10 +563,10 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, Smem<D
 
     // ---- phase 3: y = S / r_hat, first column factor c0 = max_i |y_ij| / qmax
     float mx[G];
-    scale_rows<G, false>(S, rows.rb, mx);
-    xwave_put<D>(sm, 0, w, lane, mx);
+    scale_rows<G, false>(S, rows, mx);
+    xwave_max_put<D>(sm, w, lane, mx);
     __syncthreads();
-    xwave_max<D>(sm, 0, lane, mx);
+    xwave_max<D>(sm, lane, mx);
     float c0[G], ic0[G];
     sfor<G>([&](auto gg) {
       c0[CI(gg)] = mx[CI(gg)] * IQ;
@@ -538,12 +575,12 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, Smem<D
 
     // ---- phase 4: first quantization and the least-squares column refit
     float num[G], sq[G], ic[G];
-    ls_sums<G>(S, rows.rb, ic0, num, sq);
-    xwave_put<D>(sm, 1, w, lane, num);
-    xwave_put<D>(sm, 2, w, lane, sq);
+    ls_sums<G>(S, rows, ic0, num, sq);
+    xwave_put<D>(sm, 0, w, lane, num);  // slot 0 (u) and slot 1 (readout) were last read
+    xwave_put<D>(sm, 1, w, lane, sq);   // before the barrier above
     __syncthreads();
-    xwave_sum<D>(sm, 1, lane, num);
-    xwave_sum<D>(sm, 2, lane, sq);
+    xwave_sum<D>(sm, 0, lane, num);
+    xwave_sum<D>(sm, 1, lane, sq);
     col_factor<G>(num, sq, c0, w, lane, cblk, ic, fl);
 
     // ---- phase 5: final requantization and packing
@@ -563,8 +600,8 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, Smem<D
 // GDN FP16 pivot head: the tile is stored raw in binary16, row-major
 // ---------------------------------------------------------------------------------------------
 
-template <int D, int MODE>
-__device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, int h, Smem<D>& sm) {
+template <int D, int MODE, typename SM>
+__device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, int h, SM& sm) {
   using Gm = Geo<D>;
   constexpr int G = Gm::G, R = Gm::R;
   constexpr bool kRead = MODE == FUSED || MODE == READ;
@@ -573,7 +610,7 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, int h, Smem
   const long long tile = (long long)b * A.P.H + h;
   uint8_t* seg = A.pool + (long long)b * A.P.bpr + A.P.head_off[h];
   uint16_t* hblk = reinterpret_cast<uint16_t*>(seg);
-  const Rows<D> rows(sm);
+  const Rows<SM> rows(sm);
   unsigned fl = 0;
   float S[R][G];
   float e[G], u[G], vv[G];
@@ -592,7 +629,7 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, int h, Smem
   wave_lds_sync();
   if constexpr (MODE != ENCODE) {
     if constexpr (kRead) {
-      row_dot<G>(S, [&](int r) { return rows.ra[r].k; }, u);
+      row_dot<G>(S, [&](int r) { return rows.ra[r].kr; }, u);
       xwave_put<D>(sm, 0, w, lane, u);
       __syncthreads();
       xwave_sum<D>(sm, 0, lane, u);
@@ -600,14 +637,14 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, int h, Smem
     }
     sfor<R>([&](auto rr) {
       constexpr int r = CI(rr);
-      const float bk = rows.ra[r].bk;
+      const float ar = rows.ra[r].ar, bk = rows.ra[r].bk;
       sfor<G>([&](auto gg) {
-        S[r][CI(gg)] = __builtin_fmaf(alpha, S[r][CI(gg)], bk * e[CI(gg)]);
+        S[r][CI(gg)] = __builtin_fmaf(ar, S[r][CI(gg)], bk * e[CI(gg)]);
       });
     });
     if constexpr (kRead) {
       float o[G];
-      row_dot<G>(S, [&](int r) { return rows.rb[r].q; }, o);
+      row_dot<G>(S, [&](int r) { return rows.q[r]; }, o);
       xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
       xwave_sum<D>(sm, 1, lane, o);
@@ -638,8 +675,8 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, int h, Smem
 // a row's codes sit at a uniform stream bit offset, read as a 64-bit window of the lane stream.
 // ---------------------------------------------------------------------------------------------
 
-template <int D, int MODE>
-__device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D>& sm) {
+template <int D, int MODE, typename SM>
+__device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, SM& sm) {
   using Gm = Geo<D>;
   constexpr int G = Gm::G, R = Gm::R, NT = Gm::NT;
   constexpr bool kRead = MODE == FUSED || MODE == READ;
@@ -656,7 +693,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
   const int* bitsv = A.P.bits + h * D;
   const int* posv = A.P.rowpos + h * D;
   const int* pidv = A.P.pividx + h * D;
-  const Rows<D> rows(sm);
+  const Rows<SM> rows(sm);
   unsigned fl = 0;
   float S[R][G];
   float e[G], u[G], vv[G], cc[G];
@@ -666,7 +703,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
   if constexpr (MODE != ENCODE) {
     const int n4 = nwords * 16;  // 16-byte units: nwords * 64 lanes * 4 bytes / 16
     const u32x4* g4 = reinterpret_cast<const u32x4*>(words);
-    u32x4* l4 = reinterpret_cast<u32x4*>(sm.code);
+    u32x4* l4 = reinterpret_cast<u32x4*>(sm.kc.code);
     for (int x = tid; x < n4; x += NT) l4[x] = __builtin_nontemporal_load(&g4[x]);
     if (tid < 16) l4[n4 + tid] = u32x4{0u, 0u, 0u, 0u};  // window over the last word
     sfor<G>([&](auto gg) { cc[CI(gg)] = h2f(cblk[G * lane + CI(gg)]); });
@@ -678,8 +715,8 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
     den = A.P.den[h * D + row];
     om = A.P.omega[h * D + row];
     if (lane < 32) {
-      sm.rb[row].iq = A.P.iq[h * D + row];
-      sm.qm[row] = A.P.qmax[h * D + row];
+      sm.kr.iq[row] = A.P.iq[h * D + row];
+      sm.kr.qm[row] = A.P.qmax[h * D + row];
     }
   }
   __syncthreads();
@@ -697,19 +734,18 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
       } else {
         const int bw = __builtin_amdgcn_readfirstlane(bitsv[rw]);
         const int p = __builtin_amdgcn_readfirstlane(posv[rw]);
-        const uint32_t lo = sm.code[(p >> 5) * 64 + lane];
-        const uint32_t hi = sm.code[((p >> 5) + 1) * 64 + lane];
+        const uint32_t lo = sm.kc.code[(p >> 5) * 64 + lane];
+        const uint32_t hi = sm.kc.code[((p >> 5) + 1) * 64 + lane];
         const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, p & 31);
-        const float rh = rows.ra[r].r;
         sfor<G>([&](auto gg) {
           constexpr int g = CI(gg);
           const int z = __builtin_amdgcn_sbfe((int)x, g * bw, bw);
-          S[r][g] = rh * (cc[g] * (float)z);
+          S[r][g] = cc[g] * (float)z;
         });
       }
     });
     if constexpr (kRead) {
-      row_dot<G>(S, [&](int r) { return rows.ra[r].k; }, u);
+      row_dot<G>(S, [&](int r) { return rows.ra[r].kr; }, u);
       xwave_put<D>(sm, 0, w, lane, u);
     }
   }
@@ -720,16 +756,16 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
   if constexpr (MODE != ENCODE) {
     sfor<R>([&](auto rr) {
       constexpr int r = CI(rr);
-      const float ar = rows.ra[r].a, bk = rows.ra[r].bk;
+      const float a = rows.ra[r].a, ar = rows.ra[r].ar, bk = rows.ra[r].bk;
       sfor<G>([&](auto gg) {
         constexpr int g = CI(gg);
-        const float ev = __builtin_fmaf(-ar, u[g], vv[g]);
+        const float ev = __builtin_fmaf(-a, u[g], vv[g]);
         S[r][g] = __builtin_fmaf(ar, S[r][g], bk * ev);
       });
     });
     if constexpr (kRead) {
       float o[G];
-      row_dot<G>(S, [&](int r) { return rows.rb[r].q; }, o);
+      row_dot<G>(S, [&](int r) { return rows.q[r]; }, o);
       xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
       xwave_sum<D>(sm, 1, lane, o);
@@ -748,7 +784,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
     __syncthreads();  // absT dead for every wave: the code staging area is zeroed for packing
     {
       const int n4 = nwords * 16;
-      u32x4* l4 = reinterpret_cast<u32x4*>(sm.code);
+      u32x4* l4 = reinterpret_cast<u32x4*>(sm.kc.code);
       for (int x = tid; x < n4; x += NT) l4[x] = u32x4{0u, 0u, 0u, 0u};
     }
 
@@ -765,10 +801,10 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
       }
     });
     float mx[G];
-    scale_rows<G, true>(S, rows.rb, mx);
-    xwave_put<D>(sm, 0, w, lane, mx);
+    scale_rows<G, true>(S, rows, mx);
+    xwave_max_put<D>(sm, w, lane, mx);
     __syncthreads();  // also orders the zeroing above before the packing below
-    xwave_max<D>(sm, 0, lane, mx);
+    xwave_max<D>(sm, lane, mx);
     float c0[G], ic0[G];
     sfor<G>([&](auto gg) {
       c0[CI(gg)] = mx[CI(gg)];
@@ -777,12 +813,12 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
 
     // ---- phase 4: z0 and least-squares sums
     float num[G], sq[G], ic[G];
-    ls_sums<G>(S, rows.rb, ic0, num, sq);
-    xwave_put<D>(sm, 1, w, lane, num);
-    xwave_put<D>(sm, 2, w, lane, sq);
+    ls_sums<G>(S, rows, ic0, num, sq);
+    xwave_put<D>(sm, 0, w, lane, num);
+    xwave_put<D>(sm, 1, w, lane, sq);
     __syncthreads();
-    xwave_sum<D>(sm, 1, lane, num);
-    xwave_sum<D>(sm, 2, lane, sq);
+    xwave_sum<D>(sm, 0, lane, num);
+    xwave_sum<D>(sm, 1, lane, sq);
     col_factor<G>(num, sq, c0, w, lane, cblk, ic, fl);
 
     // ---- phase 5: requantize and pack into the LDS stream (uniform positions), then copy out
@@ -792,8 +828,8 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
       bool first = true;   // the wave's first word may be shared with the previous wave
       auto flush = [&](bool shared) {
         const uint32_t lo = (uint32_t)acc;
-        if (shared) atomicOr(&sm.code[cw * 64 + lane], lo);
-        else sm.code[cw * 64 + lane] = lo;
+        if (shared) atomicOr(&sm.kc.code[cw * 64 + lane], lo);
+        else sm.kc.code[cw * 64 + lane] = lo;
       };
       sfor<R>([&](auto rr) {
         constexpr int r = CI(rr);
@@ -823,14 +859,14 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
         flush(true);  // the last word may be shared with the next wave
         // bits of a row that straddles past this word belong to word cw + 1
         const uint32_t hi = (uint32_t)(acc >> 32);
-        if (hi) atomicOr(&sm.code[(cw + 1) * 64 + lane], hi);
+        if (hi) atomicOr(&sm.kc.code[(cw + 1) * 64 + lane], hi);
       }
     }
     __syncthreads();
     {
       const int n4 = nwords * 16;
       u32x4* g4 = reinterpret_cast<u32x4*>(words);
-      const u32x4* l4 = reinterpret_cast<const u32x4*>(sm.code);
+      const u32x4* l4 = reinterpret_cast<const u32x4*>(sm.kc.code);
       for (int x = tid; x < n4; x += NT) __builtin_nontemporal_store(l4[x], &g4[x]);
     }
   }
@@ -842,8 +878,8 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, Smem<D
 // ---------------------------------------------------------------------------------------------
 
 template <int D, int MODE>
-__global__ __launch_bounds__(Geo<D>::NT) void k_gdn(StepArgs A) {
-  __shared__ Smem<D> sm;
+__global__ __launch_bounds__(Geo<D>::NT, 4) void k_gdn(StepArgs A) {
+  __shared__ Smem<D, false> sm;
   const int tile = blockIdx.x;
   const int b = tile / A.P.H, h = tile - b * A.P.H;
   switch (A.P.head_type[h]) {
@@ -857,7 +893,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void k_gdn(StepArgs A) {
 
 template <int D, int MODE>
 __global__ __launch_bounds__(Geo<D>::NT) void k_kda(StepArgs A) {
-  __shared__ Smem<D> sm;
+  __shared__ Smem<D, true> sm;
   const int tile = blockIdx.x;
   const int b = tile / A.P.H, h = tile - b * A.P.H;
   kda_tile<D, MODE>(A, b, h, sm);
