@@ -108,13 +108,23 @@ struct Geo {
   static constexpr int TOP = 3;       // tree level holding a wave's partial (log2 NQ)
 };
 
-// Per-row records, read at wave-uniform addresses (broadcast reads).
-struct RowA { float kr, ar, a, bk; };  // u (k r), update (a r, a, beta k)
-struct RowB { float q, ir, W, iq; };  // readout, row factor, least squares, column maximum
+// Per-row record, read at wave-uniform addresses (broadcast reads).  One interleaved record per
+// row keeps every field of a wave's 32 rows within ds_read's immediate offset range of a single
+// base register.  GDN rows share one gate (alpha) and one width, so they carry no a or 1/qmax.
+template <bool KDA>
+struct Row;
+template <>
+struct Row<false> {
+  float kr, ar, bk, q, ir, W;  // k r_hat, alpha r_hat, beta k, q, 1/r_hat, omega r_hat^2
+};
+template <>
+struct Row<true> {
+  float kr, ar, a, bk, q, ir, W, iq;  // ... and the row's own gate a and 1/qmax
+};
 
 template <int D, bool KDA>
-struct RowsKda {  // per-row 1/qmax and qmax of mixed-width tiles
-  float iq[D], qm[D];
+struct RowsKda {  // per-row qmax of mixed-width tiles
+  float qm[D];
 };
 template <int D>
 struct RowsKda<D, false> {};
@@ -125,7 +135,7 @@ struct CodeKda {  // code block staging of mixed-width tiles
 template <int D>
 struct CodeKda<D, false> {};
 
-// GDN tiles need 40 KB, so four workgroups fit in a CU's 160 KB: their per-row 1/qmax and qmax
+// GDN tiles need at most 40 KB, so four workgroups fit in a CU's 160 KB: their 1/qmax and qmax
 // are compile-time constants, and the column maxima pass through each wave's own (by then dead)
 // transpose section, so two cross-wave slots suffice.
 template <int D, bool KDA>
@@ -133,8 +143,7 @@ struct Smem {
   static constexpr int NW = Geo<D>::NW;
   static constexpr bool kKDA = KDA;
   static constexpr int NSLOT = KDA ? 3 : 2;
-  RowA ra[D];
-  float q[D], ir[D], W[D];
+  Row<KDA> row[D];
   [[no_unique_address]] RowsKda<D, KDA> kr;
   float red[NSLOT][NW][D];
   union {
@@ -143,23 +152,24 @@ struct Smem {
   };
 };
 
-// Wave-local views: the base index comes from threadIdx, so it stays in a VGPR and every
-// per-row read is one ds_read with an immediate offset.
+// An integer the optimizer cannot see through: each array's row base below gets its own copy,
+// so the array's address stays in its own VGPR and each access uses the instruction's small
+// immediate offset (instead of one shared base plus a large constant re-added per access).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Wave-local view of the per-row records (this wave's 32 rows; broadcast reads).
 template <typename SM>
 struct Rows {
-  const RowA* ra;
-  const float *q, *ir, *W, *iq, *qm;
+  const Row<SM::kKDA>* r;
+  const float* qm;
   __device__ __forceinline__ Rows(const SM& sm) {
     const int base = (threadIdx.x >> 6) * 32;
-    ra = sm.ra + base;
-    q = sm.q + base;
-    ir = sm.ir + base;
-    W = sm.W + base;
-    iq = qm = nullptr;
-    if constexpr (SM::kKDA) {
-      iq = sm.kr.iq + base;
-      qm = sm.kr.qm + base;
-    }
+    r = &sm.row[opaque(base)];
+    qm = nullptr;
+    if constexpr (SM::kKDA) qm = &sm.kr.qm[opaque(base)];
   }
 };
 
@@ -299,8 +309,8 @@ __device__ __forceinline__ void row_factor(SM& sm, int lane, int row, float den,
   if (!__builtin_isfinite(m)) fl |= kFlagNonfinite;
   if (lane >= 32) return;
   if (piv) {
-    sm.ir[row] = 0.0f;
-    sm.W[row] = 0.0f;
+    sm.row[row].ir = 0.0f;
+    sm.row[row].W = 0.0f;
     if (rblk) rblk[row] = 0;
     return;
   }
@@ -309,8 +319,8 @@ __device__ __forceinline__ void row_factor(SM& sm, int lane, int row, float den,
   if (is_inf16(rh)) fl |= kFlagScaleOvf;
   if (rblk) rblk[row] = rh;
   const float rf = h2f(rh);
-  sm.ir[row] = rcp0(rf);
-  sm.W[row] = (om * rf) * rf;
+  sm.row[row].ir = rcp0(rf);
+  sm.row[row].W = (om * rf) * rf;
 }
 
 // y = S * ir (in place) and the column maximum max_i |y| (GDN: one width, the 1/qmax factor
@@ -320,9 +330,9 @@ __device__ __forceinline__ void scale_rows(float (&S)[32][G], const RW& rows, fl
   sfor<G>([&](auto gg) { mx[CI(gg)] = 0.0f; });
   sfor<32>([&](auto rr) {
     constexpr int r = CI(rr);
-    const float ir = rows.ir[r];
+    const float ir = rows.r[r].ir;
     float iq = 0.0f;
-    if constexpr (KDA) iq = rows.iq[r];
+    if constexpr (KDA) iq = rows.r[r].iq;
     sfor<G>([&](auto gg) {
       constexpr int g = CI(gg);
       S[r][g] = S[r][g] * ir;
@@ -341,7 +351,7 @@ __device__ __forceinline__ void ls_sums(const float (&S)[32][G], const RW& rows,
   sfor<8>([&](auto mm) {
     constexpr int m = CI(mm);
     float W4[4];
-    sfor<4>([&](auto tt) { W4[CI(tt)] = rows.W[4 * m + CI(tt)]; });
+    sfor<4>([&](auto tt) { W4[CI(tt)] = rows.r[4 * m + CI(tt)].W; });
     sfor<G>([&](auto gg) {
       constexpr int g = CI(gg);
       float sn = 0.0f, sqv = 0.0f;
@@ -449,25 +459,26 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
     }
   }
   if (lane < 32) {
-    RowA ra{};
+    auto& rec = sm.row[row];
     // row factor: r_hat of a quantized row; 1 on pivot rows and FP16 pivot heads
     float rf = 1.0f;
     if (rblk && !(KDA && A.P.pividx[(tile % A.P.H) * D + row] >= 0)) rf = h2f(rblk[row]);
+    float a = alpha;
     if constexpr (kRead) {
       const float beta = A.beta[tile];
       const float kk = A.k[tile * D + row];
-      ra.kr = kk * rf;
-      ra.bk = beta * kk;
-      ra.a = KDA ? A.alpha[tile * D + row] : alpha;
-      sm.q[row] = A.q[tile * D + row];
+      rec.kr = kk * rf;
+      rec.bk = beta * kk;
+      if constexpr (KDA) a = A.alpha[tile * D + row];
+      rec.q = A.q[tile * D + row];
     }
     if constexpr (MODE == WRITE) {
       const float* st = A.stash + tile * 4 * D;
-      ra.a = st[row];
-      ra.bk = st[D + row];
+      a = st[row];
+      rec.bk = st[D + row];
     }
-    ra.ar = ra.a * rf;
-    sm.ra[row] = ra;
+    if constexpr (KDA) rec.a = a;
+    rec.ar = a * rf;
   }
 }
 
@@ -526,7 +537,7 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, SM& sm
       });
     });
     if constexpr (kRead) {
-      row_dot<G>(S, [&](int r) { return rows.ra[r].kr; }, u);
+      row_dot<G>(S, [&](int r) { return rows.r[r].kr; }, u);
       xwave_put<D>(sm, 0, w, lane, u);
       __syncthreads();
       xwave_sum<D>(sm, 0, lane, u);
@@ -536,20 +547,20 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, SM& sm
     // ---- phase 2: gated delta update and readout
     sfor<R>([&](auto rr) {
       constexpr int r = CI(rr);
-      const float ar = rows.ra[r].ar, bk = rows.ra[r].bk;
+      const float ar = rows.r[r].ar, bk = rows.r[r].bk;
       sfor<G>([&](auto gg) {
         S[r][CI(gg)] = __builtin_fmaf(ar, S[r][CI(gg)], bk * e[CI(gg)]);
       });
     });
     if constexpr (kRead) {
       float o[G];
-      row_dot<G>(S, [&](int r) { return rows.q[r]; }, o);
+      row_dot<G>(S, [&](int r) { return rows.r[r].q; }, o);
       xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
       xwave_sum<D>(sm, 1, lane, o);
       store_out<D>(A, tile, w, lane, o);
       if constexpr (MODE == READ) {
-        put_stash<D, false>(A, tile, w, lane, row, alpha, sm.ra[row].bk, e, u, vv);
+        put_stash<D, false>(A, tile, w, lane, row, alpha, sm.row[row].bk, e, u, vv);
         return;
       }
     }
@@ -629,7 +640,7 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, int h, SM& 
   wave_lds_sync();
   if constexpr (MODE != ENCODE) {
     if constexpr (kRead) {
-      row_dot<G>(S, [&](int r) { return rows.ra[r].kr; }, u);
+      row_dot<G>(S, [&](int r) { return rows.r[r].kr; }, u);
       xwave_put<D>(sm, 0, w, lane, u);
       __syncthreads();
       xwave_sum<D>(sm, 0, lane, u);
@@ -637,20 +648,20 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, int h, SM& 
     }
     sfor<R>([&](auto rr) {
       constexpr int r = CI(rr);
-      const float ar = rows.ra[r].ar, bk = rows.ra[r].bk;
+      const float ar = rows.r[r].ar, bk = rows.r[r].bk;
       sfor<G>([&](auto gg) {
         S[r][CI(gg)] = __builtin_fmaf(ar, S[r][CI(gg)], bk * e[CI(gg)]);
       });
     });
     if constexpr (kRead) {
       float o[G];
-      row_dot<G>(S, [&](int r) { return rows.q[r]; }, o);
+      row_dot<G>(S, [&](int r) { return rows.r[r].q; }, o);
       xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
       xwave_sum<D>(sm, 1, lane, o);
       store_out<D>(A, tile, w, lane, o);
       if constexpr (MODE == READ) {
-        put_stash<D, false>(A, tile, w, lane, row, alpha, sm.ra[row].bk, e, u, vv);
+        put_stash<D, false>(A, tile, w, lane, row, alpha, sm.row[row].bk, e, u, vv);
         return;
       }
     }
@@ -715,7 +726,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, SM& sm
     den = A.P.den[h * D + row];
     om = A.P.omega[h * D + row];
     if (lane < 32) {
-      sm.kr.iq[row] = A.P.iq[h * D + row];
+      sm.row[row].iq = A.P.iq[h * D + row];
       sm.kr.qm[row] = A.P.qmax[h * D + row];
     }
   }
@@ -745,7 +756,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, SM& sm
       }
     });
     if constexpr (kRead) {
-      row_dot<G>(S, [&](int r) { return rows.ra[r].kr; }, u);
+      row_dot<G>(S, [&](int r) { return rows.r[r].kr; }, u);
       xwave_put<D>(sm, 0, w, lane, u);
     }
   }
@@ -756,7 +767,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, SM& sm
   if constexpr (MODE != ENCODE) {
     sfor<R>([&](auto rr) {
       constexpr int r = CI(rr);
-      const float a = rows.ra[r].a, ar = rows.ra[r].ar, bk = rows.ra[r].bk;
+      const float a = rows.r[r].a, ar = rows.r[r].ar, bk = rows.r[r].bk;
       sfor<G>([&](auto gg) {
         constexpr int g = CI(gg);
         const float ev = __builtin_fmaf(-a, u[g], vv[g]);
@@ -765,13 +776,14 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, SM& sm
     });
     if constexpr (kRead) {
       float o[G];
-      row_dot<G>(S, [&](int r) { return rows.q[r]; }, o);
+      row_dot<G>(S, [&](int r) { return rows.r[r].q; }, o);
       xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
       xwave_sum<D>(sm, 1, lane, o);
       store_out<D>(A, tile, w, lane, o);
       if constexpr (MODE == READ) {
-        put_stash<D, true>(A, tile, w, lane, row, sm.ra[row].a, sm.ra[row].bk, nullptr, u, vv);
+        put_stash<D, true>(A, tile, w, lane, row, sm.row[row].a, sm.row[row].bk, nullptr,
+                           u, vv);
         return;
       }
     }

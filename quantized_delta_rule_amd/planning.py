@@ -88,3 +88,30 @@ def algorithmic_bytes(w: synth.Workload, plan: "stepq.Plan") -> int:
     a_bytes = 4 * (d if w.kind == "kda" else 1)
     io = plan.H * (3 * 4 * d + a_bytes + 4 + 4 * d)
     return w.B * (per_req + io)
+
+
+# Algorithmic ALU operations per state entry of one decode step, counted from the evaluation
+# order of the method (each binary32 multiply, add, fused multiply-add, maximum, rounding, clamp,
+# conversion and code extraction/insertion counts one; reductions over 128 rows cost
+# 128 leaves + 31 tree additions per column):
+#   dequantize 3 (extract, convert, x c_j) | k^T S 1.242 | update 2 | q^T S 1.242
+#   row magnitude 0.992 | y = S / r 1 | column maximum 1 (KDA: 2, the per-row 1/qmax)
+#   first quantization 1 | least-squares sums 3.484 | final quantization, clamp, pack 3
+# KDA adds one per entry for its per-row e = v - a_i u.  FP16 pivot rows: convert 1, k^T S,
+# update, q^T S, row magnitude, convert back 1.  Per-row and per-column work (factors and their
+# reciprocals) adds about 0.1 per entry.
+OPS_QUANT_GDN = 3 + 1.242 + 2 + 1.242 + 0.992 + 1 + 1 + 1 + 3.484 + 3 + 0.1
+OPS_QUANT_KDA = OPS_QUANT_GDN + 2
+OPS_PIVOT = 1 + 1.242 + 2 + 1.242 + 0.992 + 1 + 0.1
+
+
+def algorithmic_ops(w: synth.Workload, plan: "stepq.Plan") -> float:
+    """ALU operations one decode step of one layer performs (see the table above)."""
+    d = w.d
+    per_req = 0.0
+    for h in range(plan.H):
+        p = plan.pivot[h].astype(bool)
+        nq, npv = int((~p).sum()), int(p.sum())
+        per_req += d * (nq * (OPS_QUANT_KDA if w.kind == "kda" else OPS_QUANT_GDN)
+                        + npv * OPS_PIVOT)
+    return w.B * per_req
