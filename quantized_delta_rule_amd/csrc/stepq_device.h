@@ -72,6 +72,17 @@ __device__ __forceinline__ uint16_t f2h(float x) {
 
 __device__ __forceinline__ float rcp0(float x) { return x == 0.0f ? 0.0f : 1.0f / x; }
 
+// rcp0 of a value widened from binary16 (a stored row or column factor): v_rcp_f32 followed by
+// one Newton step with fma, y0 + y0 (1 - x y0).  The residual 1 - x y0 is exact, and for every
+// finite nonzero binary16 x the result equals the correctly rounded binary32 1/x (checked
+// exhaustively on gfx950 over all 63,486 such inputs; the raw v_rcp_f32 alone is off by one ulp
+// on 5,492 of them).  Zero and infinity map to 0, as 1/x does for infinity.
+__device__ __forceinline__ float rcp16(float x) {
+  const float y0 = __builtin_amdgcn_rcpf(x);
+  const float r = __builtin_fmaf(y0, __builtin_fmaf(-x, y0, 1.0f), y0);
+  return __builtin_amdgcn_class(x, 0x264) ? 0.0f : r;  // class bits: -inf, -0, +0, +inf
+}
+
 __device__ __forceinline__ bool is_inf16(uint16_t h) { return (h & 0x7FFFu) == 0x7C00u; }
 
 // code offset by kMagic: fma rounds the exact product y*ic once; then clamp to +-qm
@@ -160,6 +171,14 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// The same LDS address, held in one VGPR: accesses at constant distances from it then use the
+// instruction's immediate offset instead of re-adding the member's offset each time.
+template <typename T, typename SM>
+__device__ __forceinline__ T* lds_pin(SM& sm, T* p) {
+  char* const b = reinterpret_cast<char*>(&sm);
+  return reinterpret_cast<T*>(b + opaque((int)(reinterpret_cast<char*>(p) - b)));
+}
+
 // Wave-local view of the per-row records (this wave's 32 rows; broadcast reads).
 template <typename SM>
 struct Rows {
@@ -239,19 +258,20 @@ __device__ __forceinline__ void row_dot(const float (&S)[32][G], XF&& xr, float*
 template <int D, typename SM>
 __device__ __forceinline__ void xwave_put(SM& sm, int slot, int w, int lane, const float* x) {
   constexpr int G = Geo<D>::G;
-  sfor<G>([&](auto gg) { sm.red[slot][w][G * lane + CI(gg)] = x[CI(gg)]; });
+  float* const p = lds_pin(sm, &sm.red[slot][0][G * lane]);
+  sfor<G>([&](auto gg) { p[w * D + CI(gg)] = x[CI(gg)]; });
 }
 // pairwise tree over the waves' partials (rows 0-31, 32-63, ...)
 template <int D, typename SM>
 __device__ __forceinline__ void xwave_sum(SM& sm, int slot, int lane, float* x) {
   constexpr int G = Geo<D>::G, NW = Geo<D>::NW;
+  const float* const p = lds_pin(sm, &sm.red[slot][0][G * lane]);
   sfor<G>([&](auto gg) {
-    const int c = G * lane + CI(gg);
+    constexpr int g = CI(gg);
     if constexpr (NW == 2) {
-      x[CI(gg)] = sm.red[slot][0][c] + sm.red[slot][1][c];
+      x[g] = p[g] + p[D + g];
     } else {
-      x[CI(gg)] = (sm.red[slot][0][c] + sm.red[slot][1][c]) +
-                  (sm.red[slot][2][c] + sm.red[slot][3][c]);
+      x[g] = (p[g] + p[D + g]) + (p[2 * D + g] + p[3 * D + g]);
     }
   });
 }
@@ -265,17 +285,20 @@ __device__ __forceinline__ float* max_slot(SM& sm, int w) {
 template <int D, typename SM>
 __device__ __forceinline__ void xwave_max_put(SM& sm, int w, int lane, const float* x) {
   constexpr int G = Geo<D>::G;
-  float* dst = max_slot<D>(sm, w);
-  sfor<G>([&](auto gg) { dst[G * lane + CI(gg)] = x[CI(gg)]; });
+  float* const dst = lds_pin(sm, max_slot<D>(sm, w) + G * lane);
+  sfor<G>([&](auto gg) { dst[CI(gg)] = x[CI(gg)]; });
 }
 template <int D, typename SM>
 __device__ __forceinline__ void xwave_max(SM& sm, int lane, float* x) {
   constexpr int G = Geo<D>::G, NW = Geo<D>::NW;
+  // wave w' partials sit at a constant distance from wave 0's
+  const float* const p0 = lds_pin(sm, max_slot<D>(sm, 0) + G * lane);
+  constexpr int kStride = SM::kKDA ? D : 32 * 65;
   sfor<G>([&](auto gg) {
-    const int c = G * lane + CI(gg);
-    float m = max_slot<D>(sm, 0)[c];
-    sfor<NW - 1>([&](auto ww) { m = __builtin_fmaxf(m, max_slot<D>(sm, CI(ww) + 1)[c]); });
-    x[CI(gg)] = m;
+    constexpr int g = CI(gg);
+    float m = p0[g];
+    sfor<NW - 1>([&](auto ww) { m = __builtin_fmaxf(m, p0[(CI(ww) + 1) * kStride + g]); });
+    x[g] = m;
   });
 }
 
@@ -283,7 +306,7 @@ __device__ __forceinline__ void xwave_max(SM& sm, int lane, float* x) {
 template <int D, typename SM>
 __device__ __forceinline__ void put_rowabs(SM& sm, const float (&S)[32][Geo<D>::G], int lane) {
   constexpr int G = Geo<D>::G;
-  float* dst = &sm.absT[0][0][0] + (threadIdx.x >> 6) * (32 * 65) + lane;
+  float* const dst = lds_pin(sm, &sm.absT[0][0][0] + (threadIdx.x >> 6) * (32 * 65) + lane);
   sfor<32>([&](auto rr) {
     constexpr int r = CI(rr);
     float a;
@@ -301,8 +324,8 @@ template <int D, typename SM>
 __device__ __forceinline__ void row_factor(SM& sm, int lane, int row, float den, float om,
                                            bool piv, uint16_t* rblk, unsigned& fl) {
   float lv[6];
-  const float* src =
-      &sm.absT[0][0][0] + (threadIdx.x >> 6) * (32 * 65) + (lane & 31) * 65 + (lane & 32);
+  const float* const src = lds_pin(
+      sm, &sm.absT[0][0][0] + (threadIdx.x >> 6) * (32 * 65) + (lane & 31) * 65 + (lane & 32));
   sfor<32>([&](auto jj) { tree_push<CI(jj)>(lv, src[CI(jj)]); });
   const float other = __shfl_xor(lv[5], 32);
   const float m = (lane < 32 ? lv[5] + other : other + lv[5]) * (1.0f / (float)D);
@@ -319,7 +342,7 @@ __device__ __forceinline__ void row_factor(SM& sm, int lane, int row, float den,
   if (is_inf16(rh)) fl |= kFlagScaleOvf;
   if (rblk) rblk[row] = rh;
   const float rf = h2f(rh);
-  sm.row[row].ir = rcp0(rf);
+  sm.row[row].ir = rcp16(rf);
   sm.row[row].W = (om * rf) * rf;
 }
 
@@ -388,7 +411,7 @@ __device__ __forceinline__ void col_factor(const float* num, const float* sq, co
     const uint16_t ch = f2h(c1);
     if (is_inf16(ch)) fl |= kFlagScaleOvf;
     if (w == 0) cblk[G * lane + g] = ch;
-    ic[g] = rcp0(h2f(ch));
+    ic[g] = rcp16(h2f(ch));
   });
 }
 
@@ -498,7 +521,8 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, SM& sm
   const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
   const long long tile = (long long)b * A.P.H + h;
   uint8_t* seg = A.pool + (long long)b * A.P.bpr + A.P.head_off[h];
-  uint32_t* words = reinterpret_cast<uint32_t*>(seg);
+  // this lane's code words: word x of the wave's rows at wl[64 x] (one base, immediate offsets)
+  uint32_t* const wl = reinterpret_cast<uint32_t*>(seg) + (w * WPW * 64 + lane);
   uint16_t* rblk = reinterpret_cast<uint16_t*>(seg + A.P.off_r[h]);
   uint16_t* cblk = reinterpret_cast<uint16_t*>(seg + A.P.off_c[h]);
   const Rows<SM> rows(sm);
@@ -512,7 +536,7 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, SM& sm
   // ---- phase 0: code loads first (they stream from HBM), then the small per-tile inputs
   if constexpr (MODE != ENCODE) {
     sfor<WPW>([&](auto xx) {
-      wd[CI(xx)] = __builtin_nontemporal_load(&words[(w * WPW + CI(xx)) * 64 + lane]);
+      wd[CI(xx)] = __builtin_nontemporal_load(&wl[CI(xx) * 64]);
     });
     sfor<G>([&](auto gg) { cc[CI(gg)] = h2f(cblk[G * lane + CI(gg)]); });
   }
@@ -597,7 +621,7 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, SM& sm
     // ---- phase 5: final requantization and packing
     uint32_t acc = 0;
     auto store = [&](auto wi, uint32_t x) {
-      __builtin_nontemporal_store(x, &words[(w * WPW + CI(wi)) * 64 + lane]);
+      __builtin_nontemporal_store(x, &wl[CI(wi) * 64]);
     };
     sfor<R * G>([&](auto kk) {
       constexpr int K = CI(kk), r = K / G, g = K % G;
