@@ -53,6 +53,7 @@ enum { STEPQ_MODE_FUSED = 0, STEPQ_MODE_SPLIT = 1 };
 #define STEPQ_FLAG_NONFINITE 1u /* a row of an updated state was not finite               */
 #define STEPQ_FLAG_SCALE_OVF 2u /* a row or column factor overflowed binary16             */
 #define STEPQ_FLAG_PIVOT_OVF 4u /* an FP16 pivot entry overflowed binary16                */
+#define STEPQ_FLAG_BAD_SLOT 8u  /* a slot index outside [0, n_slots) other than -1          */
 
 /*
  * Plan description (Method 1: the offline precision map, pivots and impact scores).
@@ -120,6 +121,27 @@ int stepq_encode_state(stepq_plan_t plan, const float* S, void* pool, int B, voi
 int stepq_decode_step(stepq_plan_t plan, void* pool, int B, const float* q, const float* k,
                       const float* v, const float* alpha, const float* beta, float* out,
                       void* stream);
+
+/*
+ * Slot-indexed pools.  The digest runs the packed kernel inside a serving framework whose
+ * request state lives in a shared pool addressed by per-request slot indices (Method 4 and its
+ * deployment notes: the state pool grows with concurrency); these two calls take such a pool.
+ *   pool     [n_slots * bytes_per_request], 256-byte aligned: slot s is the packed state of one
+ *            request, laid out exactly as one row of the plain calls' pool.
+ *   slots    device int32 [B]: batch row b (its q, k, v, alpha, beta, out and S rows) uses
+ *            slot slots[b].  slots[b] = -1 marks a padding row: its slot, stash and out row are
+ *            not touched.  Any other value outside [0, n_slots) is skipped the same way and
+ *            raises STEPQ_FLAG_BAD_SLOT.  Two rows must not name the same slot (they would race).
+ * Everything else -- argument meaning, layout, ordering, split-mode streams -- is as for
+ * stepq_decode_step and stepq_encode_state; with slots[b] = b and n_slots = B the results are
+ * identical to theirs.  In split mode the readout kernel copies the resolved slots into a
+ * plan-owned buffer, so the caller may reuse `slots` once the work on `stream` has completed.
+ */
+int stepq_decode_step_slots(stepq_plan_t plan, void* pool, int n_slots, const int32_t* slots,
+                            int B, const float* q, const float* k, const float* v,
+                            const float* alpha, const float* beta, float* out, void* stream);
+int stepq_encode_state_slots(stepq_plan_t plan, const float* S, void* pool, int n_slots,
+                             const int32_t* slots, int B, void* stream);
 
 /* Debug decode of a pool: S_hat [B, n_heads, d_k, d_v] = r_i c_j z_ij (pivots as stored),
    r [B, n_heads, d_k] and c [B, n_heads, d_v] binary16 bit patterns, z [B, n_heads, d_k, d_v]

@@ -69,6 +69,7 @@ struct stepq_plan {
   void* dtab = nullptr;     // all device tables in one allocation
   unsigned* status = nullptr;
   float* stash = nullptr;   // split-mode hand-over
+  int* slot_stash = nullptr; // split mode: each row's resolved pool slot, for the writeback
   DevPlan dp{};
   hipStream_t side = nullptr;
   hipEvent_t ev_read = nullptr, ev_write = nullptr;
@@ -90,6 +91,7 @@ void destroy_plan(stepq_plan* p) {
   if (p->ev_write) (void)hipEventDestroy(p->ev_write);
   if (p->side) (void)hipStreamDestroy(p->side);
   if (p->stash) (void)hipFree(p->stash);
+  if (p->slot_stash) (void)hipFree(p->slot_stash);
   if (p->dtab) (void)hipFree(p->dtab);
   delete p;
 }
@@ -269,6 +271,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   if (d->mode == STEPQ_MODE_SPLIT) {
     const size_t n = (size_t)d->max_batch * H * 4 * D * sizeof(float);
     e = hipMalloc((void**)&p->stash, n);
+    if (e == hipSuccess) e = hipMalloc((void**)&p->slot_stash, (size_t)d->max_batch * sizeof(int));
     if (e != hipSuccess) {
       destroy_plan(p);
       return fail(STEPQ_ERR_OOM, "hipMalloc(%zu) for the split-mode hand-over: %s", n,
@@ -314,9 +317,18 @@ static int check_pool(const void* pool, int B) {
   return STEPQ_OK;
 }
 
-int stepq_encode_state(stepq_plan_t p, const float* S, void* pool, int B, void* stream) {
-  if (int rc = check_plan(p)) return rc;
-  if (int rc = check_pool(pool, B)) return rc;
+static int check_slots(const void* pool, int n_slots, const int32_t* slots, int B) {
+  if (B < 0) return fail(STEPQ_ERR_INVALID_ARG, "B must be >= 0");
+  if (B == 0) return STEPQ_OK;
+  if (n_slots < 1) return fail(STEPQ_ERR_INVALID_ARG, "n_slots must be >= 1");
+  if (!slots) return fail(STEPQ_ERR_INVALID_ARG, "slots is NULL");
+  return check_pool(pool, n_slots);
+}
+
+namespace {
+
+int encode_impl(stepq_plan_t p, const float* S, void* pool, int n_slots, const int32_t* slots,
+                int B, void* stream) {
   if (B > 0 && !S) return fail(STEPQ_ERR_INVALID_ARG, "S is NULL");
   if (p->mode == STEPQ_MODE_SPLIT && B > p->max_batch)
     return fail(STEPQ_ERR_INVALID_ARG, "B = %d exceeds max_batch %d", B, p->max_batch);
@@ -329,15 +341,15 @@ int stepq_encode_state(stepq_plan_t p, const float* S, void* pool, int B, void* 
   a.B = B;
   a.S_in = S;
   a.stash = p->stash;
-  HIP_TRY(launch_step(p->kind, ENCODE, a, s));
+  a.slots = slots;
+  a.n_slots = n_slots;
+  if (B > 0) HIP_TRY(launch_step(p->kind, ENCODE, a, s));
   return ok();
 }
 
-int stepq_decode_step(stepq_plan_t p, void* pool, int B, const float* q, const float* k,
-                      const float* v, const float* alpha, const float* beta, float* out,
-                      void* stream) {
-  if (int rc = check_plan(p)) return rc;
-  if (int rc = check_pool(pool, B)) return rc;
+int decode_impl(stepq_plan_t p, void* pool, int n_slots, const int32_t* slots, int B,
+                const float* q, const float* k, const float* v, const float* alpha,
+                const float* beta, float* out, void* stream) {
   if (B > 0 && (!q || !k || !v || !alpha || !beta || !out))
     return fail(STEPQ_ERR_INVALID_ARG, "q, k, v, alpha, beta and out must be non-NULL");
   if (p->mode == STEPQ_MODE_SPLIT && B > p->max_batch)
@@ -356,20 +368,57 @@ int stepq_decode_step(stepq_plan_t p, void* pool, int B, const float* q, const f
   a.beta = beta;
   a.out = out;
   a.stash = p->stash;
+  a.slots = slots;
+  a.n_slots = n_slots;
   if (p->mode == STEPQ_MODE_FUSED) {
     HIP_TRY(launch_step(p->kind, FUSED, a, s));
     return ok();
   }
-  // split: readout on the caller's stream; refit + pack on the side stream once it is done
+  // split: readout on the caller's stream; refit + pack on the side stream once it is done.
+  // The readout kernel records each row's resolved slot, so the writeback never reads the
+  // caller's slot array (which the caller may reuse once `stream` has run).
   HIP_TRY(wait_writeback(p, s));
+  if (slots) a.slot_out = p->slot_stash;
   HIP_TRY(launch_step(p->kind, READ, a, s));
   HIP_TRY(hipEventRecord(p->ev_read, s));
   HIP_TRY(hipStreamWaitEvent(p->side, p->ev_read, 0));
   if (p->spin_cycles > 0) HIP_TRY(launch_spin(p->spin_cycles, p->side));
+  if (slots) a.slots = p->slot_stash;
   HIP_TRY(launch_step(p->kind, WRITE, a, p->side));
   HIP_TRY(hipEventRecord(p->ev_write, p->side));
   p->write_pending = true;
   return ok();
+}
+
+}  // namespace
+
+int stepq_encode_state(stepq_plan_t p, const float* S, void* pool, int B, void* stream) {
+  if (int rc = check_plan(p)) return rc;
+  if (int rc = check_pool(pool, B)) return rc;
+  return encode_impl(p, S, pool, B, nullptr, B, stream);
+}
+
+int stepq_encode_state_slots(stepq_plan_t p, const float* S, void* pool, int n_slots,
+                             const int32_t* slots, int B, void* stream) {
+  if (int rc = check_plan(p)) return rc;
+  if (int rc = check_slots(pool, n_slots, slots, B)) return rc;
+  return encode_impl(p, S, pool, n_slots, slots, B, stream);
+}
+
+int stepq_decode_step(stepq_plan_t p, void* pool, int B, const float* q, const float* k,
+                      const float* v, const float* alpha, const float* beta, float* out,
+                      void* stream) {
+  if (int rc = check_plan(p)) return rc;
+  if (int rc = check_pool(pool, B)) return rc;
+  return decode_impl(p, pool, B, nullptr, B, q, k, v, alpha, beta, out, stream);
+}
+
+int stepq_decode_step_slots(stepq_plan_t p, void* pool, int n_slots, const int32_t* slots,
+                            int B, const float* q, const float* k, const float* v,
+                            const float* alpha, const float* beta, float* out, void* stream) {
+  if (int rc = check_plan(p)) return rc;
+  if (int rc = check_slots(pool, n_slots, slots, B)) return rc;
+  return decode_impl(p, pool, n_slots, slots, B, q, k, v, alpha, beta, out, stream);
 }
 
 int stepq_unpack_debug(stepq_plan_t p, const void* pool, int B, float* S_hat, uint16_t* r,

@@ -43,7 +43,8 @@ namespace dev {
 
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-constexpr unsigned kFlagNonfinite = 1u, kFlagScaleOvf = 2u, kFlagPivotOvf = 4u;
+constexpr unsigned kFlagNonfinite = 1u, kFlagScaleOvf = 2u, kFlagPivotOvf = 4u,
+                   kFlagBadSlot = 8u;
 
 template <int N, typename F>
 __device__ __forceinline__ void sfor(F&& f) {
@@ -510,7 +511,7 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
 // ---------------------------------------------------------------------------------------------
 
 template <int D, int MODE, int BITS, typename SM>
-__device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, SM& sm) {
+__device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slot, int h, SM& sm) {
   using Gm = Geo<D>;
   constexpr int G = Gm::G, R = Gm::R;
   constexpr int WPW = R * G * BITS / 32;  // code words per lane for one wave's rows
@@ -520,7 +521,7 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, SM& sm
   constexpr bool kWrite = MODE != READ;                   // refits and packs
   const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
   const long long tile = (long long)b * A.P.H + h;
-  uint8_t* seg = A.pool + (long long)b * A.P.bpr + A.P.head_off[h];
+  uint8_t* seg = A.pool + slot * A.P.bpr + A.P.head_off[h];
   // this lane's code words: word x of the wave's rows at wl[64 x] (one base, immediate offsets)
   uint32_t* const wl = reinterpret_cast<uint32_t*>(seg) + (w * WPW * 64 + lane);
   uint16_t* rblk = reinterpret_cast<uint16_t*>(seg + A.P.off_r[h]);
@@ -636,14 +637,14 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, int h, SM& sm
 // ---------------------------------------------------------------------------------------------
 
 template <int D, int MODE, typename SM>
-__device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, int h, SM& sm) {
+__device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, long long slot, int h, SM& sm) {
   using Gm = Geo<D>;
   constexpr int G = Gm::G, R = Gm::R;
   constexpr bool kRead = MODE == FUSED || MODE == READ;
   constexpr bool kWrite = MODE != READ;
   const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
   const long long tile = (long long)b * A.P.H + h;
-  uint8_t* seg = A.pool + (long long)b * A.P.bpr + A.P.head_off[h];
+  uint8_t* seg = A.pool + slot * A.P.bpr + A.P.head_off[h];
   uint16_t* hblk = reinterpret_cast<uint16_t*>(seg);
   const Rows<SM> rows(sm);
   unsigned fl = 0;
@@ -711,7 +712,7 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, int h, SM& 
 // ---------------------------------------------------------------------------------------------
 
 template <int D, int MODE, typename SM>
-__device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, SM& sm) {
+__device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slot, int h, SM& sm) {
   using Gm = Geo<D>;
   constexpr int G = Gm::G, R = Gm::R, NT = Gm::NT;
   constexpr bool kRead = MODE == FUSED || MODE == READ;
@@ -719,7 +720,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, SM& sm
   const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
   const int tid = threadIdx.x;
   const long long tile = (long long)b * A.P.H + h;
-  uint8_t* seg = A.pool + (long long)b * A.P.bpr + A.P.head_off[h];
+  uint8_t* seg = A.pool + slot * A.P.bpr + A.P.head_off[h];
   uint32_t* words = reinterpret_cast<uint32_t*>(seg);
   uint16_t* pblk = reinterpret_cast<uint16_t*>(seg + A.P.off_piv[h]);
   uint16_t* rblk = reinterpret_cast<uint16_t*>(seg + A.P.off_r[h]);
@@ -913,17 +914,34 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, int h, SM& sm
 // kernels
 // ---------------------------------------------------------------------------------------------
 
+// Pool slot of batch row b (uniform over the workgroup): b itself, or slots[b] for a
+// slot-indexed pool; -1 = skip the row.  Thread 0 of each request's head-0 tile records the
+// resolved slot for the split-mode writeback and raises the bad-slot flag.
+template <int MODE>
+__device__ __forceinline__ long long pool_slot(const StepArgs& A, int b, int h) {
+  if (!A.slots) return b;
+  const int s = A.slots[b];
+  const bool valid = s >= 0 && s < A.n_slots;
+  if (h == 0 && threadIdx.x == 0) {
+    if (MODE == READ) A.slot_out[b] = valid ? s : -1;
+    if (MODE != WRITE && !valid && s != -1) atomicOr(A.P.status, kFlagBadSlot);
+  }
+  return valid ? s : -1;
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(Geo<D>::NT, 4) void k_gdn(StepArgs A) {
   __shared__ Smem<D, false> sm;
   const int tile = blockIdx.x;
   const int b = tile / A.P.H, h = tile - b * A.P.H;
+  const long long slot = pool_slot<MODE>(A, b, h);
+  if (slot < 0) return;
   switch (A.P.head_type[h]) {
-    case 2: gdn_tile<D, MODE, 2>(A, b, h, sm); break;
-    case 4: gdn_tile<D, MODE, 4>(A, b, h, sm); break;
-    case 6: gdn_tile<D, MODE, 6>(A, b, h, sm); break;
-    case 8: gdn_tile<D, MODE, 8>(A, b, h, sm); break;
-    default: pivot_tile<D, MODE>(A, b, h, sm); break;
+    case 2: gdn_tile<D, MODE, 2>(A, b, slot, h, sm); break;
+    case 4: gdn_tile<D, MODE, 4>(A, b, slot, h, sm); break;
+    case 6: gdn_tile<D, MODE, 6>(A, b, slot, h, sm); break;
+    case 8: gdn_tile<D, MODE, 8>(A, b, slot, h, sm); break;
+    default: pivot_tile<D, MODE>(A, b, slot, h, sm); break;
   }
 }
 
@@ -932,7 +950,9 @@ __global__ __launch_bounds__(Geo<D>::NT) void k_kda(StepArgs A) {
   __shared__ Smem<D, true> sm;
   const int tile = blockIdx.x;
   const int b = tile / A.P.H, h = tile - b * A.P.H;
-  kda_tile<D, MODE>(A, b, h, sm);
+  const long long slot = pool_slot<MODE>(A, b, h);
+  if (slot < 0) return;
+  kda_tile<D, MODE>(A, b, slot, h, sm);
 }
 
 // Debug decode: one workgroup per tile, same lane/row mapping, any head type.

@@ -49,6 +49,12 @@ struct StepArgs {
   float* out;
   float* stash;      // split-mode hand-over, [B*H][4*D]
   const float* S_in; // ENCODE input [B*H][D][D]
+  // Slot-indexed pools: batch row b uses pool slot slots[b] (nullptr: slot b).  A value outside
+  // [0, n_slots) skips the row (-1 silently, anything else also raises the bad-slot flag).
+  // READ writes each row's resolved slot (-1 = skipped) to slot_out[b] for the WRITE kernel.
+  const int* slots;
+  int n_slots;
+  int* slot_out;
 };
 
 // Launchers (stepq_kernels.hip).  kind: 0 = GDN, 1 = KDA.

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libstepq.so")
 
 GDN, KDA = 0, 1
 FUSED, SPLIT = 0, 1
-FLAG_NONFINITE, FLAG_SCALE_OVF, FLAG_PIVOT_OVF = 1, 2, 4
+FLAG_NONFINITE, FLAG_SCALE_OVF, FLAG_PIVOT_OVF, FLAG_BAD_SLOT = 1, 2, 4, 8
 
 _lib = None
 
@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
         "stepq_head_segment": (i, [P, i, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
         "stepq_encode_state": (i, [P, P, P, i, P]),
         "stepq_decode_step": (i, [P, P, i, P, P, P, P, P, P, P]),
+        "stepq_encode_state_slots": (i, [P, P, P, i, P, i, P]),
+        "stepq_decode_step_slots": (i, [P, P, i, P, i, P, P, P, P, P, P, P]),
         "stepq_unpack_debug": (i, [P, P, i, P, P, P, P, P]),
         "stepq_get_status": (i, [P, ctypes.POINTER(ctypes.c_uint32), i]),
         "stepq_sync": (i, [P]),
@@ -169,19 +171,42 @@ class Plan:
         _check(lib().stepq_encode_state(self._h, sp, self._pool(pool, B), int(B),
                                         _stream_ptr(stream)), "encode_state")
 
-    def step(self, pool, B, q, k, v, alpha, beta, out, stream=None):
+    def _step_args(self, B, q, k, v, alpha, beta, out):
         import torch
-        self._batch(B)
         n = B * self.H * self.d
         na = B * self.H * (self.d if self.kind == KDA else 1)
         f = torch.float32
-        args = [_dev_tensor(q, "q", f, n, self.device), _dev_tensor(k, "k", f, n, self.device),
+        return [_dev_tensor(q, "q", f, n, self.device), _dev_tensor(k, "k", f, n, self.device),
                 _dev_tensor(v, "v", f, n, self.device),
                 _dev_tensor(alpha, "alpha", f, na, self.device),
                 _dev_tensor(beta, "beta", f, B * self.H, self.device),
                 _dev_tensor(out, "out", f, n, self.device)]
+
+    def step(self, pool, B, q, k, v, alpha, beta, out, stream=None):
+        self._batch(B)
+        args = self._step_args(B, q, k, v, alpha, beta, out)
         _check(lib().stepq_decode_step(self._h, self._pool(pool, B), int(B), *args,
                                        _stream_ptr(stream)), "decode_step")
+
+    # -- slot-indexed pools: batch row b uses pool slot slots[b] (-1 = padding row) --------
+    def _slots(self, slots, B):
+        import torch
+        return _dev_tensor(slots, "slots", torch.int32, B, self.device)
+
+    def encode_slots(self, S, pool, n_slots, slots, B, stream=None):
+        import torch
+        self._batch(B)
+        sp = _dev_tensor(S, "S", torch.float32, B * self.H * self.d * self.d, self.device)
+        _check(lib().stepq_encode_state_slots(self._h, sp, self._pool(pool, n_slots),
+                                              int(n_slots), self._slots(slots, B), int(B),
+                                              _stream_ptr(stream)), "encode_state_slots")
+
+    def step_slots(self, pool, n_slots, slots, B, q, k, v, alpha, beta, out, stream=None):
+        self._batch(B)
+        args = self._step_args(B, q, k, v, alpha, beta, out)
+        _check(lib().stepq_decode_step_slots(self._h, self._pool(pool, n_slots), int(n_slots),
+                                             self._slots(slots, B), int(B), *args,
+                                             _stream_ptr(stream)), "decode_step_slots")
 
     def unpack(self, pool, B, stream=None):
         """Returns S_hat [B,H,d,d] f32, r [B,H,d] u16 bits, c [B,H,d] u16 bits, z [B,H,d,d] i8."""
