@@ -178,6 +178,18 @@ int stepq_lifetime_weights(const double* l_u, int n, int H, double* L_out);
 int stepq_row_impact_accumulate(int n, int d, const float* q, const float* k, const float* a,
                                 const float* beta, double* acc);
 
+/* Row impact on the device (Method 2), for calibration before any plan exists.  For every head
+   h of one layer and each of the B requests of one step: g = A^T q with
+   A = Diag(a)(I - beta k k^T); acc[h*d + i] += sum over the requests of g_i^2, in binary64
+   (requests in index order, so the result is deterministic).
+     kind   STEPQ_KIND_GDN (alpha [B, n_heads]) or STEPQ_KIND_KDA (alpha [B, n_heads, d]);
+     q, k   [B, n_heads, d] fp32 device;  beta [B, n_heads] fp32 device;
+     acc    [n_heads * d] binary64 device, added to (zero it before the first step).
+   d in {64, 128}.  omega = acc / (requests x steps accumulated).  Enqueued on `stream` on the
+   current device. */
+int stepq_row_impact_gpu(int kind, int n_heads, int d, int B, const float* q, const float* k,
+                         const float* alpha, const float* beta, double* acc, void* stream);
+
 /* The n_pivots units of largest risk (e.g. L_u d_u(b_max)); ties to the lower index.
    out_idx [n_pivots] ascending. */
 int stepq_select_pivots(const double* risk, int n, int n_pivots, int32_t* out_idx);

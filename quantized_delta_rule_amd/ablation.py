@@ -28,7 +28,7 @@ import sys
 
 import numpy as np
 
-from . import planning, stepq, synth
+from . import planning, reference, stepq, synth
 
 
 def variant_plans(w: synth.Workload, layer: int = 0):
@@ -47,37 +47,6 @@ def variant_plans(w: synth.Workload, layer: int = 0):
     return plans
 
 
-def fp32_step(S, q, k, v, a, beta):
-    """FP32-state reference step on tiles S [N, d_k, d_v] in place; returns o [N, d_v].
-    a: per-row gate [N, d_k]; A = Diag(a)(I - beta k k^T)."""
-    u = (S * k[:, :, None]).sum(1)                          # S^T k
-    e = v[:, None, :] - a[:, :, None] * u[:, None, :]       # v - a_i u
-    S.mul_(a[:, :, None]).add_((beta[:, None] * k)[:, :, None] * e)
-    return (S * q[:, :, None]).sum(1)
-
-
-def warm_state(w: synth.Workload, layer: int, dev):
-    """Initial states [B*H, d, d]: w.warmup FP32 steps from zero."""
-    import torch
-    d = w.d
-    S = torch.zeros((w.B * w.H, d, d), dtype=torch.float32, device=dev)
-    for s in range(w.warmup):
-        x = _dev(synth.step_inputs(w, layer, s, "warmup"), w, dev)
-        fp32_step(S, x["q"], x["k"], x["v"], x["a"], x["beta"])
-    return S
-
-
-def _dev(x, w, dev):
-    """Step inputs on the device, flattened over (request, head): q, k, v, a [B*H, d], beta
-    [B*H], and alpha as the decode call takes it."""
-    import torch
-    d = w.d
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    return {"q": t(x["q"].reshape(-1, d)), "k": t(x["k"].reshape(-1, d)),
-            "v": t(x["v"].reshape(-1, d)), "a": t(synth.alpha_rows(w, x["alpha"]).reshape(-1, d)),
-            "beta": t(x["beta"].reshape(-1)), "alpha": t(x["alpha"])}
-
-
 def _rel(a, b):
     return float((a - b).double().norm() / max(float(b.double().norm()), 1e-300))
 
@@ -91,7 +60,7 @@ def drift(w: synth.Workload, steps: int, layer: int = 0, variants=None, device=0
     plans = variant_plans(w, layer)
     if variants is not None:
         plans = {k: v for k, v in plans.items() if k in variants}
-    S_ref = warm_state(w, layer, dev)
+    S_ref = reference.warm_state(w, layer, dev)
     runs = {}
     for name, (bits, piv, om) in plans.items():
         p = stepq.Plan(kind, bits, piv, om, device=device)
@@ -101,8 +70,8 @@ def drift(w: synth.Workload, steps: int, layer: int = 0, variants=None, device=0
     B, H, d = w.B, w.H, w.d
     out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
     for s in range(steps):
-        x = _dev(synth.step_inputs(w, layer, s, "decode"), w, dev)
-        o_ref = fp32_step(S_ref, x["q"], x["k"], x["v"], x["a"], x["beta"]).reshape(B, H, d)
+        x = reference.device_inputs(synth.step_inputs(w, layer, s, "decode"), w, dev)
+        o_ref = reference.fp32_step(S_ref, x["q"], x["k"], x["v"], x["a"], x["beta"]).reshape(B, H, d)
         for name, (p, pool, errs) in runs.items():
             p.step(pool, B, x["q"], x["k"], x["v"], x["alpha"], x["beta"], out)
             errs.append(_rel(out, o_ref))

@@ -25,8 +25,8 @@ HIPCC_FLAGS = [
 ]
 
 
-SOURCES = ("stepq_k128_gdn.hip", "stepq_k128_kda.hip", "stepq_k64.hip", "stepq_api.cpp",
-           "stepq_offline.cpp")
+SOURCES = ("stepq_k128_gdn.hip", "stepq_k128_kda.hip", "stepq_k64.hip", "stepq_calib.hip",
+           "stepq_api.cpp", "stepq_offline.cpp")
 OBJDIR = os.path.join(HERE, "_build")
 
 

@@ -454,6 +454,18 @@ int stepq_get_status(stepq_plan_t p, uint32_t* flags, int reset) {
   return ok();
 }
 
+int stepq_row_impact_gpu(int kind, int n_heads, int d, int B, const float* q, const float* k,
+                         const float* alpha, const float* beta, double* acc, void* stream) {
+  if (kind != STEPQ_KIND_GDN && kind != STEPQ_KIND_KDA)
+    return fail(STEPQ_ERR_INVALID_ARG, "kind must be STEPQ_KIND_GDN or STEPQ_KIND_KDA");
+  if (n_heads < 1 || B < 0) return fail(STEPQ_ERR_INVALID_ARG, "n_heads >= 1 and B >= 0 required");
+  if (d != 64 && d != 128) return fail(STEPQ_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  if (!acc || (B > 0 && (!q || !k || !alpha || !beta)))
+    return fail(STEPQ_ERR_INVALID_ARG, "q, k, alpha, beta and acc must be non-NULL");
+  HIP_TRY(launch_row_impact(kind, n_heads, d, B, q, k, alpha, beta, acc, (hipStream_t)stream));
+  return ok();
+}
+
 // Test hook: a bounded spin of `cycles` clocks on the side stream before each split-mode
 // writeback, to show that the next step's readout waits for it.
 int stepq_debug_side_delay(stepq_plan_t p, long long cycles) {

@@ -61,6 +61,8 @@ struct StepArgs {
 hipError_t launch_step(int kind, Mode mode, const StepArgs& a, hipStream_t s);
 hipError_t launch_unpack(const DevPlan& P, const uint8_t* pool, int B, float* S, uint16_t* r,
                          uint16_t* c, int8_t* z, hipStream_t s);
+hipError_t launch_row_impact(int kind, int H, int D, int B, const float* q, const float* k,
+                             const float* alpha, const float* beta, double* acc, hipStream_t s);
 hipError_t launch_spin(long long cycles, hipStream_t s);
 
 }  // namespace stepq

@@ -10,12 +10,20 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import stepq, synth
+from . import reference, stepq, synth
 
 
-def omega(w: synth.Workload, layer: int, phase: str = "warmup", steps: int | None = None):
-    """Row impact [H, d] accumulated by the library over the given input steps."""
-    steps = w.warmup if steps is None else steps
+def _calib_phase(w: synth.Workload):
+    """Input stream and step count the row impact is estimated on."""
+    return ("calib", w.calib_steps) if w.calib_steps else ("warmup", w.warmup)
+
+
+def omega(w: synth.Workload, layer: int, phase: str | None = None, steps: int | None = None):
+    """Row impact [H, d] accumulated by the library's host planner over the given input steps
+    (default: the workload's calibration stream)."""
+    dphase, dsteps = _calib_phase(w)
+    phase = dphase if phase is None else phase
+    steps = dsteps if steps is None else steps
     acc = np.zeros((w.H, w.d))
     n = 0
     for s in range(steps):
@@ -26,6 +34,61 @@ def omega(w: synth.Workload, layer: int, phase: str = "warmup", steps: int | Non
                                         acc[h])
         n += w.B
     return (acc / n).astype(np.float32)
+
+
+def omega_gpu(w: synth.Workload, layer: int, phase: str | None = None,
+              steps: int | None = None, device: int = 0):
+    """The same row impact [H, d], accumulated on the device (stepq_row_impact_gpu)."""
+    import torch
+    dphase, dsteps = _calib_phase(w)
+    phase = dphase if phase is None else phase
+    steps = dsteps if steps is None else steps
+    dev = torch.device(f"cuda:{device}")
+    acc = torch.zeros(w.H * w.d, dtype=torch.float64, device=dev)
+    kind = stepq.GDN if w.kind == "gdn" else stepq.KDA
+    for s in range(steps):
+        x = {k: torch.from_numpy(v).to(dev) for k, v in synth.step_inputs(w, layer, s, phase).items()}
+        stepq.row_impact_gpu(kind, x["q"], x["k"], x["alpha"], x["beta"], acc)
+    return (acc / (w.B * steps)).to(torch.float32).cpu().numpy().reshape(w.H, w.d)
+
+
+def measured_distortion_gpu(w: synth.Workload, layer: int, omega_l, n_req: int = 8,
+                            samples=(32, 64), device: int = 0):
+    """d(b) per key row [H, d, len(choices)]: the squared reconstruction error summed over the
+    row, of the uniform-width-b plan (no pivots) encoded and decoded by the library's kernels,
+    averaged over calibration states (n_req requests run from zero on the calibration stream,
+    states at the sample steps).  Method 1: the allocation's reconstruction distortion d_u(b),
+    measured rather than modelled."""
+    import torch
+    dev = torch.device(f"cuda:{device}")
+    kind = stepq.GDN if w.kind == "gdn" else stepq.KDA
+    H, d = w.H, w.d
+    n_req = min(n_req, w.B)
+    states = reference.calib_states(w, layer, dev, n_req, samples)
+    du = torch.zeros((H, d, len(w.choices)), dtype=torch.float64, device=dev)
+    for ci, b in enumerate(w.choices):
+        plan = stepq.Plan(kind, np.full((H, d), b, np.int8), np.zeros((H, d), np.uint8), omega_l,
+                          device=device)
+        pool = plan.alloc_pool(n_req)
+        for S in states:
+            plan.encode(S, pool, n_req)
+            S_hat = plan.unpack(pool, n_req)[0].reshape(n_req * H, d, d)
+            err = ((S.double() - S_hat.double()) ** 2).sum(-1)        # [n_req*H, d]
+            du[:, :, ci] += err.reshape(n_req, H, d).sum(0)
+        if plan.status() != 0:
+            raise RuntimeError(f"width {b}: status flags raised while measuring d_u")
+        plan.close()
+    return (du / (len(states) * n_req)).cpu().numpy()
+
+
+def calibrate(w: synth.Workload, device: int = 0):
+    """Row impact [layers, H, d] and the measured distortion table [units, choices] (units:
+    layers*H heads for GDN, layers*H*d key rows for KDA), both from the library's kernels."""
+    om = np.stack([omega_gpu(w, l, device=device) for l in range(w.layers)])
+    du = np.stack([measured_distortion_gpu(w, l, om[l], device=device) for l in range(w.layers)])
+    if w.kind == "gdn":
+        du = du.sum(axis=2)                       # a head's distortion: sum over its rows
+    return om, du.reshape(-1, len(w.choices))
 
 
 def allocate(w: synth.Workload, distortion=None):
@@ -51,8 +114,12 @@ def allocate(w: synth.Workload, distortion=None):
 
 
 def plan_arrays(w: synth.Workload, omegas=None, distortion=None):
-    """(bits, pivot, omega), each [layers, H, d], for the workload."""
+    """(bits, pivot, omega), each [layers, H, d], for the workload.  A workload with a measured
+    distortion table is calibrated on the device first (calibrate)."""
     Lr, H, d = w.layers, w.H, w.d
+    if w.du == "measured" and distortion is None and w.alloc != "fixed":
+        om_c, distortion = calibrate(w)
+        omegas = om_c if omegas is None else omegas
     if omegas is None:
         omegas = np.stack([omega(w, l) for l in range(Lr)])
     bits = np.zeros((Lr, H, d), np.int8)

@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
         "stepq_last_error": (ctypes.c_char_p, []),
         "stepq_lifetime_weights": (i, [P, i, i, P]),
         "stepq_row_impact_accumulate": (i, [i, i, P, P, P, P, P]),
+        "stepq_row_impact_gpu": (i, [i, i, i, i, P, P, P, P, P, P]),
         "stepq_select_pivots": (i, [P, i, i, P]),
         "stepq_alloc_mcdp": (i, [P, i, P, i, ctypes.c_long, P, ctypes.POINTER(d)]),
         "stepq_alloc_lagrangian": (i, [P, P, P, i, P, i, d, i, P, ctypes.POINTER(d)]),
@@ -254,6 +255,23 @@ def row_impact_accumulate(q, k, a, beta, acc):
                                              beta.ctypes.data, acc.ctypes.data),
            "row_impact_accumulate")
     return acc
+
+
+def row_impact_gpu(kind, q, k, alpha, beta, acc, stream=None):
+    """acc [H*d] float64 (device) += sum over requests of g_i^2, g = A^T q, for one step of one
+    layer: q, k [B, H, d], alpha [B, H] (GDN) or [B, H, d] (KDA), beta [B, H] (device fp32)."""
+    import torch
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, d]")
+    B, H, d = q.shape
+    dev = q.device.index
+    f = torch.float32
+    na = B * H * (d if kind == KDA else 1)
+    args = [_dev_tensor(q, "q", f, B * H * d, dev), _dev_tensor(k, "k", f, B * H * d, dev),
+            _dev_tensor(alpha, "alpha", f, na, dev), _dev_tensor(beta, "beta", f, B * H, dev),
+            _dev_tensor(acc, "acc", torch.float64, H * d, dev)]
+    _check(lib().stepq_row_impact_gpu(int(kind), int(H), int(d), int(B), *args,
+                                      _stream_ptr(stream)), "row_impact_gpu")
 
 
 def select_pivots(risk, n_pivots):

@@ -45,6 +45,7 @@ class Workload:
     fixed_bits: tuple = ()     # per-head widths for alloc == "fixed" (0 = FP16 pivot head)
     calib_steps: int = 0       # calibration steps for omega (KDA); 0 = use the warm-up
     horizon: int = 512         # H of the lifetime weight
+    gates: str = "independent" # GDN gates: "independent" of l_u, or "lifetime" (log alpha ~ l_u)
 
     @property
     def tiles_per_layer(self) -> int:
@@ -70,6 +71,11 @@ WORKLOADS = {
     5: Workload(5, "gdn6-stress-256x12x48", "gdn", B=256, layers=12, H=48, d=128, steps=128,
                 warmup=16, choices=(4, 6, 8), nominal=6, n_pivots=_pivots(32, 2304, 576),
                 alloc="mcdp", split=True),
+    # the allocation's own premise: each head's gates follow its lifetime l_u, and the
+    # distortion table is measured on calibration states (used by the ablation report)
+    6: Workload(6, "gdn6-lifetime-70x48", "gdn", B=70, layers=1, H=48, d=128, steps=256,
+                warmup=16, choices=(4, 6, 8), nominal=6, n_pivots=_pivots(32, 2304, 48),
+                alloc="mcdp", du="measured", gates="lifetime"),
 }
 
 
@@ -125,7 +131,13 @@ def step_inputs(w: Workload, layer: int, step: int, phase: str = "decode"):
     beta = 1.0 / (1.0 + np.exp(-g.standard_normal((w.B, w.H))))
     if w.kind == "gdn":
         x = g.normal(-4.0, 0.5, size=(w.B, w.H))
-        alpha = np.exp(-np.logaddexp(0.0, x))
+        if w.gates == "lifetime":
+            # log alpha = l_u * exp(0.1 z), z ~ N(0, 1): per-head mean log gate l_u, so a head's
+            # errors persist for about 1/|l_u| steps, as the lifetime weight assumes
+            l_u = plan_tables(w)[0][layer * w.H:(layer + 1) * w.H]
+            alpha = np.exp(l_u[None, :] * np.exp(0.1 * (x + 4.0) / 0.5))
+        else:
+            alpha = np.exp(-np.logaddexp(0.0, x))
     else:
         alpha = g.uniform(0.8, 1.0, size=shp)
     rho, gam = geometry(w, layer)

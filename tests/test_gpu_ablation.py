@@ -25,19 +25,20 @@ def gpu():
 
 @pytest.mark.parametrize("wid", [2, 4])
 def test_fp32_reference_matches_oracle(gpu, wid):
-    """The drift report's FP32 recurrence (plain torch) against the oracle's FP32-state run on
+    """The FP32 recurrence of the product side (plain torch: initial and calibration states, the
+    drift reference) against the oracle's FP32-state run on
     the same inputs: both sum in binary32 in different orders, so they agree to ~1e-6."""
     torch = gpu
-    from quantized_delta_rule_amd import ablation
+    from quantized_delta_rule_amd import reference
     w = dataclasses.replace(synth.WORKLOADS[wid], B=2, H=3, warmup=12)
     dev = torch.device("cuda:0")
-    S_t = ablation.warm_state(w, 0, dev)
+    S_t = reference.warm_state(w, 0, dev)
     S_o = P.warm_state(w, 0)
     assert P.rel_l2(S_t.cpu().numpy(), S_o) < 1e-5
     for s in range(6):
         xh = synth.step_inputs(w, 0, s, "decode")
-        x = ablation._dev(xh, w, dev)
-        o_t = ablation.fp32_step(S_t, x["q"], x["k"], x["v"], x["a"], x["beta"]).cpu().numpy()
+        x = reference.device_inputs(xh, w, dev)
+        o_t = reference.fp32_step(S_t, x["q"], x["k"], x["v"], x["a"], x["beta"]).cpu().numpy()
         a_rows = synth.alpha_rows(w, xh["alpha"])
         for t in range(w.B * w.H):
             b, h = divmod(t, w.H)
