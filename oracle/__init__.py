@@ -73,10 +73,10 @@ def lib() -> ctypes.CDLL:
         L.orc_unpack.argtypes = [i, i, P, P, P, P, P, P, P]
         L.orc_encode.restype = i
         L.orc_encode.argtypes = [i, i, P, P, P, P, P, P, P]
-        L.orc_tile_step.restype = i
-        L.orc_tile_step.argtypes = [i, i, P, P, P, P, P, P, P, P, f, P, P, P, P]
-        L.orc_fp32_step.argtypes = [i, i, P, P, P, P, P, f, P]
-        L.orc_fp32_run.argtypes = [i, i, i, i, P, P, P, P, l, P, l, P, P]
+        L.orc_tile_step_o.restype = i
+        L.orc_tile_step_o.argtypes = [i, i, P, P, P, P, P, P, P, P, f, P, P, P, P, i]
+        L.orc_fp32_step_o.argtypes = [i, i, P, P, P, P, P, f, P, i]
+        L.orc_fp32_run_o.argtypes = [i, i, i, i, P, P, P, P, l, P, l, P, P, i]
         _lib = L
     return _lib
 
@@ -121,15 +121,21 @@ def dot(x, y) -> np.float32:
 # one head of the plan and its packed segment
 # ----------------------------------------------------------------------------------------------
 
-class Head:
-    """Static description of one head: per-row bits, pivot flags and row impact omega."""
+DELTA_FIRST, DECAY_FIRST = 0, 1   # gate orders: A = Diag(a)(I - b k k^T) or (I - b k k^T) Diag(a)
 
-    def __init__(self, bits, pivot, omega, dv=None):
+
+class Head:
+    """Static description of one head: per-row bits, pivot flags and row impact omega, and the
+    gate order of its update (DELTA_FIRST, the literal A_t = Diag(a)(I - beta k k^T), or
+    DECAY_FIRST, A_t = (I - beta k k^T) Diag(a))."""
+
+    def __init__(self, bits, pivot, omega, dv=None, order=DELTA_FIRST):
         self.bits = _c(bits, np.int8)
         self.pivot = _c(pivot, np.uint8)
         self.omega = _c(omega, np.float32)
         self.dk = self.bits.size
         self.dv = self.dk if dv is None else dv
+        self.order = int(order)
 
     @property
     def seg_bytes(self) -> int:
@@ -169,9 +175,10 @@ class Head:
         S = np.empty(self.dk * self.dv, np.float32) if want_state else None
         pre = np.empty(self.dk * self.dv, np.float64) if want_state else None
         fl = ctypes.c_uint32(0)
-        rc = lib().orc_tile_step(self.dk, self.dv, _p(self.bits), _p(self.pivot),
+        rc = lib().orc_tile_step_o(self.dk, self.dv, _p(self.bits), _p(self.pivot),
                                  _p(self.omega), _p(seg), _p(q), _p(k), _p(v), _p(a),
-                                 float(beta), _p(out), _p(S), _p(pre), ctypes.addressof(fl))
+                                 float(beta), _p(out), _p(S), _p(pre), ctypes.addressof(fl),
+                                 self.order)
         if rc != 0:
             raise ValueError("corrupt code (-2^(b-1)) in segment")
         if want_state:
@@ -179,18 +186,19 @@ class Head:
         return out
 
 
-def fp32_step(S, q, k, v, a, beta):
+def fp32_step(S, q, k, v, a, beta, order=DELTA_FIRST):
     """FP32-state step on one tile in place; returns the readout."""
     dk, dv = S.shape
     q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
     a = _c(np.broadcast_to(np.asarray(a, np.float32), (dk,)), np.float32)
     out = np.empty(dv, np.float32)
     assert S.dtype == np.float32 and S.flags.c_contiguous
-    lib().orc_fp32_step(dk, dv, _p(S), _p(q), _p(k), _p(v), _p(a), float(beta), _p(out))
+    lib().orc_fp32_step_o(dk, dv, _p(S), _p(q), _p(k), _p(v), _p(a), float(beta), _p(out),
+                          int(order))
     return out
 
 
-def fp32_run(S, q, k, v, a, beta, threads=8, want_out=False):
+def fp32_run(S, q, k, v, a, beta, threads=8, want_out=False, order=DELTA_FIRST):
     """FP32-state steps on a batch of tiles.
 
     S: [N, dk, dv] float32 (updated in place).  q, k, v: [T, N, d]; a: [T, N, dk]; beta: [T, N].
@@ -211,10 +219,10 @@ def fp32_run(S, q, k, v, a, beta, threads=8, want_out=False):
         if n == 0:
             return
         b = np.ascontiguousarray(beta[:, t0:t1])
-        lib().orc_fp32_run(dk, dv, n, T, S[t0:].ctypes.data, q[:, t0:].ctypes.data,
+        lib().orc_fp32_run_o(dk, dv, n, T, S[t0:].ctypes.data, q[:, t0:].ctypes.data,
                            k[:, t0:].ctypes.data, v[:, t0:].ctypes.data, N * dv,
                            a[:, t0:].ctypes.data, N * dk, _p(b),
-                           None if out is None else out[:, t0:].ctypes.data)
+                           None if out is None else out[:, t0:].ctypes.data, int(order))
     with ThreadPoolExecutor(nth) as ex:
         list(ex.map(lambda ab: work(*ab), zip(bounds[:-1], bounds[1:])))
     return out
@@ -232,13 +240,17 @@ def lifetime_weight(l_u, H: int) -> np.ndarray:
     return np.array([np.sum(np.exp(2.0 * j * lu)) for lu in l_u.ravel()]).reshape(l_u.shape)
 
 
-def row_impact(q, k, a, beta) -> np.ndarray:
-    """omega_i = E[g_i^2] with g = A^T q = a*q - beta k (k . (a*q)) for A = Diag(a)(I - b k k^T)
-    (Method 2).  q, k, a: [n, dk] samples of one head; beta: [n].  Mean over samples."""
+def row_impact(q, k, a, beta, order=DELTA_FIRST) -> np.ndarray:
+    """omega_i = E[g_i^2] with g = A^T q (Method 2): for A = Diag(a)(I - b k k^T),
+    g = a*q - beta k (k . (a*q)); for A = (I - b k k^T) Diag(a), g = a * (q - beta k (k . q)).
+    q, k, a: [n, dk] samples of one head; beta: [n].  Mean over samples."""
     q, k, a = (np.asarray(x, np.float64) for x in (q, k, a))
     beta = np.asarray(beta, np.float64)
-    aq = a * q
-    g = aq - (beta * np.sum(k * aq, axis=-1))[:, None] * k
+    if order == DECAY_FIRST:
+        g = a * (q - (beta * np.sum(k * q, axis=-1))[:, None] * k)
+    else:
+        aq = a * q
+        g = aq - (beta * np.sum(k * aq, axis=-1))[:, None] * k
     return np.mean(g * g, axis=0)
 
 

@@ -22,7 +22,8 @@
  * The scale formulas (r_i = (mean_j|S_ij| + 1e-8)/(1 + omega_i/mean omega), c_j initialised to
  * max_i|S_ij/r_i|/qmax, one omega-weighted least-squares refit with z fixed, symmetric
  * round-half-even with qmax = 2^(b-1)-1) and the gate A_t = Diag(a)(I - beta k k^T) are the
- * readings this build takes where the pages leave the step open.
+ * readings this build takes where the pages leave the step open; the other gate order,
+ * A_t = (I - beta k k^T) Diag(a), is available as a plan option (ORC_DECAY_FIRST).
  *
  * Arithmetic: IEEE binary32, round to nearest even, subnormals kept.  Every operation is rounded
  * on its own; a fused multiply-add appears only where fmaf() is written.  A code is the
@@ -381,18 +382,30 @@ done:
    The row factor enters through the row coefficients k_i f_i and a_i f_i:
      u_j = dot_i(k_i f_i, X_ij);  e = fma(-a_i, u_j, v_j);  S_ij = fma(a_i f_i, X_ij, (beta k_i) e)
    With a = 1 and beta = 0 this returns S_ij = f_i X_ij rounded once: the decoded state. */
+/* Gate orders of A_t (both readings of the digest's "A_t contains the retention gate and the
+   Delta update"):
+     ORC_DELTA_FIRST  A = Diag(a)(I - beta k k^T): the delta update, then the decay of each row
+                      (the literal reading; S_t = a_i (S - beta k u^T)_i + beta k_i v^T with
+                      u = S^T k);
+     ORC_DECAY_FIRST  A = (I - beta k k^T) Diag(a): the rows decay first and the delta update sees
+                      the decayed state (u = (Diag(a) S)^T k, e = v - u, one e per column).
+   For a scalar gate (GDN) the two are the same map; their binary32 results differ in rounding. */
+#define ORC_DELTA_FIRST 0
+#define ORC_DECAY_FIRST 1
+
 static void delta_update_readout(int dk, int dv, float* S, const float* f, const float* q,
                                  const float* k, const float* v, const float* a, float beta,
-                                 float* out) {
+                                 float* out, int order) {
   float* u = (float*)malloc(sizeof(float) * dv);
   float* kf = (float*)malloc(sizeof(float) * dk);
-  for (int i = 0; i < dk; i++) kf[i] = k[i] * f[i];
+  /* row coefficient of the key projection: k_i f_i, or k_i (a_i f_i) once the rows decayed */
+  for (int i = 0; i < dk; i++) kf[i] = order == ORC_DECAY_FIRST ? k[i] * (a[i] * f[i]) : k[i] * f[i];
   for (int j = 0; j < dv; j++) u[j] = dot_fixed(kf, 1, S + j, dv, dk);
   for (int i = 0; i < dk; i++) {
     float bk = beta * k[i], af = a[i] * f[i];
     for (int j = 0; j < dv; j++) {
       long e = (long)i * dv + j;
-      float ev = fmaf(-a[i], u[j], v[j]);
+      float ev = order == ORC_DECAY_FIRST ? v[j] - u[j] : fmaf(-a[i], u[j], v[j]);
       S[e] = fmaf(af, S[e], bk * ev);
     }
   }
@@ -424,13 +437,14 @@ static int decode_factored(int dk, int dv, const int8_t* bits, const uint8_t* pi
 /* Decode step of one (request, head) tile, in place on seg.  a has dk entries (all equal for
    GDN).  S_upd (optional) receives the updated fp32 state before requantization, pre (optional)
    the final pre-rounding values.  Returns 0, or -1 on a corrupt code. */
-int orc_tile_step(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const float* omega,
-                  uint8_t* seg, const float* q, const float* k, const float* v, const float* a,
-                  float beta, float* out, float* S_upd, double* pre, uint32_t* flags) {
+int orc_tile_step_o(int dk, int dv, const int8_t* bits, const uint8_t* pivot,
+                    const float* omega, uint8_t* seg, const float* q, const float* k,
+                    const float* v, const float* a, float beta, float* out, float* S_upd,
+                    double* pre, uint32_t* flags, int order) {
   float* S = (float*)malloc(sizeof(float) * dk * dv);
   float* f = (float*)malloc(sizeof(float) * dk);
   int rc = decode_factored(dk, dv, bits, pivot, seg, S, f);
-  delta_update_readout(dk, dv, S, f, q, k, v, a, beta, out);
+  delta_update_readout(dk, dv, S, f, q, k, v, a, beta, out, order);
   free(f);
   if (S_upd) memcpy(S_upd, S, sizeof(float) * dk * dv);
   orc_encode(dk, dv, bits, pivot, omega, S, seg, pre, flags);
@@ -438,13 +452,25 @@ int orc_tile_step(int dk, int dv, const int8_t* bits, const uint8_t* pivot, cons
   return rc;
 }
 
+int orc_tile_step(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const float* omega,
+                  uint8_t* seg, const float* q, const float* k, const float* v, const float* a,
+                  float beta, float* out, float* S_upd, double* pre, uint32_t* flags) {
+  return orc_tile_step_o(dk, dv, bits, pivot, omega, seg, q, k, v, a, beta, out, S_upd, pre,
+                         flags, ORC_DELTA_FIRST);
+}
+
 /* FP32-state mode: the same update and readout on an unquantized state (warm-up, drift). */
-void orc_fp32_step(int dk, int dv, float* S, const float* q, const float* k, const float* v,
-                   const float* a, float beta, float* out) {
+void orc_fp32_step_o(int dk, int dv, float* S, const float* q, const float* k, const float* v,
+                     const float* a, float beta, float* out, int order) {
   float* f = (float*)malloc(sizeof(float) * dk);
   for (int i = 0; i < dk; i++) f[i] = 1.0f;
-  delta_update_readout(dk, dv, S, f, q, k, v, a, beta, out);
+  delta_update_readout(dk, dv, S, f, q, k, v, a, beta, out, order);
   free(f);
+}
+
+void orc_fp32_step(int dk, int dv, float* S, const float* q, const float* k, const float* v,
+                   const float* a, float beta, float* out) {
+  orc_fp32_step_o(dk, dv, S, q, k, v, a, beta, out, ORC_DELTA_FIRST);
 }
 
 /* ------------------------------------------------------------------------------------------ */
@@ -462,15 +488,22 @@ void orc_f16_to_f32_n(const uint16_t* h, float* x, long n) {
 /* T fp32-state steps on ntiles independent tiles.  Tile t, step s reads q/k/v at
    base + s*step_stride + t*dv (and a at a + s*a_step + t*dk, beta at beta[s*nt + t]) and writes
    out (if not NULL) likewise. */
-void orc_fp32_run(int dk, int dv, int ntiles, int T, float* S, const float* q, const float* k,
-                  const float* v, long step_stride, const float* a, long a_step,
-                  const float* beta, float* out) {
+void orc_fp32_run_o(int dk, int dv, int ntiles, int T, float* S, const float* q,
+                    const float* k, const float* v, long step_stride, const float* a,
+                    long a_step, const float* beta, float* out, int order) {
   for (int s = 0; s < T; s++)
     for (int t = 0; t < ntiles; t++) {
       long o = (long)s * step_stride + (long)t * dv;
       float tmp[256];
-      orc_fp32_step(dk, dv, S + (long)t * dk * dv, q + o, k + o, v + o,
-                    a + (long)s * a_step + (long)t * dk, beta[(long)s * ntiles + t],
-                    out ? out + o : tmp);
+      orc_fp32_step_o(dk, dv, S + (long)t * dk * dv, q + o, k + o, v + o,
+                      a + (long)s * a_step + (long)t * dk, beta[(long)s * ntiles + t],
+                      out ? out + o : tmp, order);
     }
+}
+
+void orc_fp32_run(int dk, int dv, int ntiles, int T, float* S, const float* q, const float* k,
+                  const float* v, long step_stride, const float* a, long a_step,
+                  const float* beta, float* out) {
+  orc_fp32_run_o(dk, dv, ntiles, T, S, q, k, v, step_stride, a, a_step, beta, out,
+                 ORC_DELTA_FIRST);
 }

@@ -94,3 +94,15 @@ def test_row_impact_closed_forms(orc):
         A = np.diag(a[t]) @ (np.eye(d) - beta[t] * np.outer(k[t], k[t]))
         ref += (A.T @ q[t]) ** 2
     assert np.allclose(om, ref / n, rtol=1e-12)
+    # the other gate order, A = (I - beta k k^T) Diag(a)
+    om2 = orc.row_impact(q, k, a, beta, order=orc.DECAY_FIRST)
+    ref2 = np.zeros(d)
+    for t in range(n):
+        A = (np.eye(d) - beta[t] * np.outer(k[t], k[t])) @ np.diag(a[t])
+        ref2 += (A.T @ q[t]) ** 2
+    assert np.allclose(om2, ref2 / n, rtol=1e-12)
+    assert not np.allclose(om2, om, rtol=1e-3)
+    # a scalar gate commutes with the delta update: both orders give the same impact
+    a1 = np.repeat(a[:, :1], d, axis=1)
+    assert np.allclose(orc.row_impact(q, k, a1, beta, order=orc.DECAY_FIRST),
+                       orc.row_impact(q, k, a1, beta), rtol=1e-12)

@@ -53,27 +53,50 @@ def test_orthonormal_retrieval_fp32_state(orc):
             assert rel <= 1e-5, (m, i, rel)
 
 
+@pytest.mark.parametrize("order", [0, 1])
 @pytest.mark.parametrize("kda", [False, True])
-def test_update_matches_binary64_formula(orc, kda):
+def test_update_matches_binary64_formula(orc, kda, order):
+    """Both gate orders against the matrix formula in binary64: order 0 (delta update first,
+    A = Diag(a)(I - beta k k^T)) and order 1 (rows decay first, A = (I - beta k k^T) Diag(a))."""
     g = np.random.default_rng(23)
     d = 128
     head, seg = _make(orc, g, d, kda)
+    head.order = order
     S_hat, _, _, _ = head.unpack(seg)
     q, k, v = _unit(g, d), _unit(g, d), g.standard_normal(d).astype(np.float32)
     a = (g.uniform(0.8, 1.0, d) if kda else np.full(d, 0.97)).astype(np.float32)
     beta = np.float32(0.6)
     out, S_upd, _, _ = head.step(seg.copy(), q, k, v, a, beta, want_state=True)
     S64, k64, q64 = S_hat.astype(np.float64), k.astype(np.float64), q.astype(np.float64)
-    A = np.diag(a.astype(np.float64)) @ (np.eye(d) - float(beta) * np.outer(k64, k64))
+    Da = np.diag(a.astype(np.float64))
+    P_ = np.eye(d) - float(beta) * np.outer(k64, k64)
+    A, A_other = (Da @ P_, P_ @ Da) if order == 0 else (P_ @ Da, Da @ P_)
     ref = A @ S64 + float(beta) * np.outer(k64, v.astype(np.float64))
     scale = np.abs(S64).max() + 1
     assert np.max(np.abs(S_upd - ref)) <= 1e-5 * scale
-    # the other gate order, (I - beta k k^T) Diag(a), is measurably different for KDA
+    # the other gate order is measurably different for a per-row gate (KDA)
     if kda:
-        alt = (np.eye(d) - float(beta) * np.outer(k64, k64)) @ np.diag(a) @ S64 \
-            + float(beta) * np.outer(k64, v)
+        alt = A_other @ S64 + float(beta) * np.outer(k64, v)
         assert np.max(np.abs(S_upd - alt)) > 1e-3 * np.max(np.abs(ref - S64))
     assert np.max(np.abs(out - ref.T @ q64)) <= 1e-5 * scale
+
+
+def test_gate_orders_agree_for_a_scalar_gate(orc):
+    """With one gate for all rows (GDN) the two orders are the same map: their binary32 results
+    differ only by rounding, and FP32-state runs stay together."""
+    g = np.random.default_rng(29)
+    d = 64
+    S1 = (g.standard_normal((d, d)) * 0.3).astype(np.float32)
+    S2 = S1.copy()
+    for t in range(20):
+        q, k, v = _unit(g, d), _unit(g, d), g.standard_normal(d).astype(np.float32)
+        a = np.full(d, g.uniform(0.9, 1.0), np.float32)
+        beta = np.float32(g.uniform(0.2, 0.9))
+        o1 = orc.fp32_step(S1, q, k, v, a, beta, order=0)
+        o2 = orc.fp32_step(S2, q, k, v, a, beta, order=1)
+        assert np.max(np.abs(o1 - o2)) <= 1e-5 * (np.abs(o1).max() + 1)
+    assert np.max(np.abs(S1 - S2)) <= 1e-5 * (np.abs(S1).max() + 1)
+    assert not np.array_equal(S1, S2)  # the rounding does differ
 
 
 @pytest.mark.parametrize("kda", [False, True])
