@@ -48,6 +48,8 @@ enum {
 
 enum { STEPQ_KIND_GDN = 0, STEPQ_KIND_KDA = 1 };
 enum { STEPQ_MODE_FUSED = 0, STEPQ_MODE_SPLIT = 1 };
+/* gate order of A_t (see stepq_plan_desc.order) */
+enum { STEPQ_ORDER_DELTA_FIRST = 0, STEPQ_ORDER_DECAY_FIRST = 1 };
 
 /* status word bits (stepq_get_status) */
 #define STEPQ_FLAG_NONFINITE 1u /* a row of an updated state was not finite               */
@@ -71,6 +73,11 @@ enum { STEPQ_MODE_FUSED = 0, STEPQ_MODE_SPLIT = 1 };
  *             (Method 4: scale fitting and packed writeback overlap later layers).
  *   max_batch largest B any call will pass (sizes the split-mode hand-over buffer).
  *   device    HIP device ordinal the plan lives on.
+ *   order     how A_t composes the gate and the delta update (Background: A_t holds both).
+ *             STEPQ_ORDER_DELTA_FIRST: A_t = Diag(a)(I - beta k k^T), the reading this library
+ *             takes by default.  STEPQ_ORDER_DECAY_FIRST: A_t = (I - beta k k^T) Diag(a), the rows
+ *             decay before the delta update (the key projection sees the decayed state).  For
+ *             GDN's scalar gate the two are one map and differ only in rounding.
  * All host arrays are copied; the caller may free them after the call.
  */
 typedef struct {
@@ -83,6 +90,7 @@ typedef struct {
   int mode;
   int max_batch;
   int device;
+  int order;
 } stepq_plan_desc;
 
 /* Validate desc, build the packed layout and upload the plan tables to the device. */
@@ -172,23 +180,27 @@ const char* stepq_last_error(void);
    steps; l_u = mean log retention gate of unit u, <= 0). */
 int stepq_lifetime_weights(const double* l_u, int n, int H, double* L_out);
 
-/* Accumulate row impact (Method 2): for n samples of one head, g = A^T q with
-   A = Diag(a)(I - beta k k^T); acc[i] += sum over samples of g_i^2.  q, k, a: [n, d] float,
-   beta: [n] float.  omega = acc / (number of samples) once all samples are in. */
+/* Accumulate row impact (Method 2): for n samples of one head, g = A^T q with A as selected by
+   order (STEPQ_ORDER_DELTA_FIRST: Diag(a)(I - beta k k^T), g = a*q - beta k (k . (a*q));
+   STEPQ_ORDER_DECAY_FIRST: (I - beta k k^T) Diag(a), g = a*(q - beta k (k . q)));
+   acc[i] += sum over samples of g_i^2.  q, k, a: [n, d] float, beta: [n] float.
+   omega = acc / (number of samples) once all samples are in. */
 int stepq_row_impact_accumulate(int n, int d, const float* q, const float* k, const float* a,
-                                const float* beta, double* acc);
+                                const float* beta, int order, double* acc);
 
 /* Row impact on the device (Method 2), for calibration before any plan exists.  For every head
-   h of one layer and each of the B requests of one step: g = A^T q with
-   A = Diag(a)(I - beta k k^T); acc[h*d + i] += sum over the requests of g_i^2, in binary64
-   (requests in index order, so the result is deterministic).
+   h of one layer and each of the B requests of one step: g = A^T q with A as selected by order
+   (as for stepq_row_impact_accumulate); acc[h*d + i] += sum over the requests of g_i^2, in
+   binary64 (requests in index order, so the result is deterministic).
      kind   STEPQ_KIND_GDN (alpha [B, n_heads]) or STEPQ_KIND_KDA (alpha [B, n_heads, d]);
+     order  STEPQ_ORDER_DELTA_FIRST or STEPQ_ORDER_DECAY_FIRST;
      q, k   [B, n_heads, d] fp32 device;  beta [B, n_heads] fp32 device;
      acc    [n_heads * d] binary64 device, added to (zero it before the first step).
    d in {64, 128}.  omega = acc / (requests x steps accumulated).  Enqueued on `stream` on the
    current device. */
-int stepq_row_impact_gpu(int kind, int n_heads, int d, int B, const float* q, const float* k,
-                         const float* alpha, const float* beta, double* acc, void* stream);
+int stepq_row_impact_gpu(int kind, int order, int n_heads, int d, int B, const float* q,
+                         const float* k, const float* alpha, const float* beta, double* acc,
+                         void* stream);
 
 /* The n_pivots units of largest risk (e.g. L_u d_u(b_max)); ties to the lower index.
    out_idx [n_pivots] ascending. */

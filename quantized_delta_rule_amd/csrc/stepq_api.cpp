@@ -121,6 +121,8 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
     return fail(STEPQ_ERR_INVALID_ARG, "bits, pivot and omega must be non-NULL");
   if (d->mode != STEPQ_MODE_FUSED && d->mode != STEPQ_MODE_SPLIT)
     return fail(STEPQ_ERR_INVALID_ARG, "mode must be STEPQ_MODE_FUSED or STEPQ_MODE_SPLIT");
+  if (d->order != STEPQ_ORDER_DELTA_FIRST && d->order != STEPQ_ORDER_DECAY_FIRST)
+    return fail(STEPQ_ERR_INVALID_ARG, "order must be STEPQ_ORDER_DELTA_FIRST or STEPQ_ORDER_DECAY_FIRST");
   if (d->mode == STEPQ_MODE_SPLIT && d->max_batch < 1)
     return fail(STEPQ_ERR_INVALID_ARG, "split mode needs max_batch >= 1");
   int ndev = 0;
@@ -251,6 +253,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   DevPlan& dp = p->dp;
   dp.H = H;
   dp.D = D;
+  dp.order = d->order;
   dp.bpr = p->bpr;
   dp.head_off = (const long long*)at(i_hoff);
   dp.head_type = (const int*)at(i_type);
@@ -454,15 +457,19 @@ int stepq_get_status(stepq_plan_t p, uint32_t* flags, int reset) {
   return ok();
 }
 
-int stepq_row_impact_gpu(int kind, int n_heads, int d, int B, const float* q, const float* k,
-                         const float* alpha, const float* beta, double* acc, void* stream) {
+int stepq_row_impact_gpu(int kind, int order, int n_heads, int d, int B, const float* q,
+                         const float* k, const float* alpha, const float* beta, double* acc,
+                         void* stream) {
   if (kind != STEPQ_KIND_GDN && kind != STEPQ_KIND_KDA)
     return fail(STEPQ_ERR_INVALID_ARG, "kind must be STEPQ_KIND_GDN or STEPQ_KIND_KDA");
+  if (order != STEPQ_ORDER_DELTA_FIRST && order != STEPQ_ORDER_DECAY_FIRST)
+    return fail(STEPQ_ERR_INVALID_ARG, "order must be STEPQ_ORDER_DELTA_FIRST or STEPQ_ORDER_DECAY_FIRST");
   if (n_heads < 1 || B < 0) return fail(STEPQ_ERR_INVALID_ARG, "n_heads >= 1 and B >= 0 required");
   if (d != 64 && d != 128) return fail(STEPQ_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
   if (!acc || (B > 0 && (!q || !k || !alpha || !beta)))
     return fail(STEPQ_ERR_INVALID_ARG, "q, k, alpha, beta and acc must be non-NULL");
-  HIP_TRY(launch_row_impact(kind, n_heads, d, B, q, k, alpha, beta, acc, (hipStream_t)stream));
+  HIP_TRY(launch_row_impact(kind, order, n_heads, d, B, q, k, alpha, beta, acc,
+                            (hipStream_t)stream));
   return ok();
 }
 

@@ -255,6 +255,18 @@ __device__ __forceinline__ void row_dot(const float (&S)[32][G], XF&& xr, float*
   sfor<G>([&](auto gg) { res[CI(gg)] = lv[CI(gg)][3]; });
 }
 
+// Per-column error of the delta update with one gate for all rows: e = v - alpha u (the delta
+// update sees the undecayed state), or e = v - u when the rows decayed first (the key
+// projection already carries the gate).
+template <int G>
+__device__ __forceinline__ void col_error(int order, float alpha, const float* u, const float* vv,
+                                          float* e) {
+  sfor<G>([&](auto gg) {
+    constexpr int g = CI(gg);
+    e[g] = order ? vv[g] - u[g] : __builtin_fmaf(-alpha, u[g], vv[g]);
+  });
+}
+
 // Cross-wave combination of this lane's per-wave partials (red[slot][w][col]).
 template <int D, typename SM>
 __device__ __forceinline__ void xwave_put(SM& sm, int slot, int w, int lane, const float* x) {
@@ -424,8 +436,9 @@ __device__ __forceinline__ void store_out(const StepArgs& A, long long tile, int
 }
 
 // Split-mode hand-over of the update factors: a_i, beta k_i per row (lane L < 32 of each
-// wave); e_j (GDN) or u_j and v_j (KDA) per column (wave 0).
-template <int D, bool KDA>
+// wave); per column (wave 0) either e_j (UV false: GDN, or any gate decaying the rows first) or
+// u_j and v_j (UV true: per-row gate applied after the delta update, e_ij = v_j - a_i u_j).
+template <int D, bool UV>
 __device__ __forceinline__ void put_stash(const StepArgs& A, long long tile, int w, int lane,
                                           int row, float a_row, float bk_row, const float* e,
                                           const float* u, const float* vv) {
@@ -438,7 +451,7 @@ __device__ __forceinline__ void put_stash(const StepArgs& A, long long tile, int
   if (w == 0) {
     sfor<G>([&](auto gg) {
       constexpr int g = CI(gg);
-      if constexpr (KDA) {
+      if constexpr (UV) {
         st[2 * D + G * lane + g] = u[g];
         st[3 * D + G * lane + g] = vv[g];
       } else {
@@ -459,8 +472,10 @@ __device__ __forceinline__ void load_state(const StepArgs& A, long long tile, in
 }
 
 // Per-tile inputs of a step: row records (lanes 0..31 of each wave fill their wave's rows),
-// per-column v or the hand-over.  Returns alpha (GDN) and fills vv / e / u.
-template <int D, int MODE, bool KDA, typename SM>
+// per-column v or the hand-over.  Returns alpha (GDN) and fills vv / e / u.  UV: the hand-over
+// carries u and v (per-row e) instead of e.  The key-projection coefficient of a row is k_i r_i,
+// or k_i (a_i r_i) when the gate decays the rows before the delta update (plan order 1).
+template <int D, int MODE, bool KDA, bool UV = KDA, typename SM>
 __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long tile,
                                             int lane, int row, const uint16_t* rblk,
                                             float& alpha, float* vv, float* e, float* u) {
@@ -472,13 +487,13 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
   }
   if constexpr (MODE == WRITE) {
     const float* st = A.stash + tile * 4 * D;
-    if constexpr (KDA) {
+    if constexpr (UV) {
       sfor<G>([&](auto gg) {
         u[CI(gg)] = st[2 * D + G * lane + CI(gg)];
         vv[CI(gg)] = st[3 * D + G * lane + CI(gg)];
       });
     } else {
-      alpha = st[0];
+      if constexpr (!KDA) alpha = st[0];
       sfor<G>([&](auto gg) { e[CI(gg)] = st[2 * D + G * lane + CI(gg)]; });
     }
   }
@@ -491,9 +506,10 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
     if constexpr (kRead) {
       const float beta = A.beta[tile];
       const float kk = A.k[tile * D + row];
-      rec.kr = kk * rf;
-      rec.bk = beta * kk;
       if constexpr (KDA) a = A.alpha[tile * D + row];
+      const float ar = a * rf;
+      rec.kr = A.P.order ? kk * ar : kk * rf;
+      rec.bk = beta * kk;
       rec.q = A.q[tile * D + row];
     }
     if constexpr (MODE == WRITE) {
@@ -566,7 +582,7 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
       xwave_put<D>(sm, 0, w, lane, u);
       __syncthreads();
       xwave_sum<D>(sm, 0, lane, u);
-      sfor<G>([&](auto gg) { e[CI(gg)] = __builtin_fmaf(-alpha, u[CI(gg)], vv[CI(gg)]); });
+      col_error<G>(A.P.order, alpha, u, vv, e);
     }
 
     // ---- phase 2: gated delta update and readout
@@ -669,7 +685,7 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, long long s
       xwave_put<D>(sm, 0, w, lane, u);
       __syncthreads();
       xwave_sum<D>(sm, 0, lane, u);
-      sfor<G>([&](auto gg) { e[CI(gg)] = __builtin_fmaf(-alpha, u[CI(gg)], vv[CI(gg)]); });
+      col_error<G>(A.P.order, alpha, u, vv, e);
     }
     sfor<R>([&](auto rr) {
       constexpr int r = CI(rr);
@@ -711,12 +727,16 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, long long s
 // a row's codes sit at a uniform stream bit offset, read as a 64-bit window of the lane stream.
 // ---------------------------------------------------------------------------------------------
 
-template <int D, int MODE, typename SM>
+// ORDER 0: A = Diag(a)(I - beta k k^T), a per-row error e_ij = v_j - a_i u_j.  ORDER 1:
+// A = (I - beta k k^T) Diag(a): the key projection carries the gate, one error e_j = v_j - u_j
+// per column.
+template <int D, int MODE, int ORDER, typename SM>
 __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slot, int h, SM& sm) {
   using Gm = Geo<D>;
   constexpr int G = Gm::G, R = Gm::R, NT = Gm::NT;
   constexpr bool kRead = MODE == FUSED || MODE == READ;
   constexpr bool kWrite = MODE != READ;
+  constexpr bool kUV = ORDER == 0;  // split-mode hand-over carries u and v (per-row error)
   const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
   const int tid = threadIdx.x;
   const long long tile = (long long)b * A.P.H + h;
@@ -744,7 +764,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     if (tid < 16) l4[n4 + tid] = u32x4{0u, 0u, 0u, 0u};  // window over the last word
     sfor<G>([&](auto gg) { cc[CI(gg)] = h2f(cblk[G * lane + CI(gg)]); });
   }
-  load_inputs<D, MODE, true>(A, sm, tile, lane, row, MODE != ENCODE ? rblk : nullptr, alpha, vv,
+  load_inputs<D, MODE, true, kUV>(A, sm, tile, lane, row, MODE != ENCODE ? rblk : nullptr, alpha, vv,
                              e, u);
   float den = 1.0f, om = 0.0f;
   if constexpr (kWrite) {
@@ -786,7 +806,10 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     }
   }
   __syncthreads();  // code block reads done (LDS reused below), cross-wave u staged
-  if constexpr (kRead) xwave_sum<D>(sm, 0, lane, u);
+  if constexpr (kRead) {
+    xwave_sum<D>(sm, 0, lane, u);
+    if constexpr (!kUV) sfor<G>([&](auto gg) { e[CI(gg)] = vv[CI(gg)] - u[CI(gg)]; });
+  }
 
   // ---- phase 2: update, readout
   if constexpr (MODE != ENCODE) {
@@ -795,7 +818,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
       const float a = rows.r[r].a, ar = rows.r[r].ar, bk = rows.r[r].bk;
       sfor<G>([&](auto gg) {
         constexpr int g = CI(gg);
-        const float ev = __builtin_fmaf(-a, u[g], vv[g]);
+        const float ev = kUV ? __builtin_fmaf(-a, u[g], vv[g]) : e[g];
         S[r][g] = __builtin_fmaf(ar, S[r][g], bk * ev);
       });
     });
@@ -807,8 +830,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
       xwave_sum<D>(sm, 1, lane, o);
       store_out<D>(A, tile, w, lane, o);
       if constexpr (MODE == READ) {
-        put_stash<D, true>(A, tile, w, lane, row, sm.row[row].a, sm.row[row].bk, nullptr,
-                           u, vv);
+        put_stash<D, kUV>(A, tile, w, lane, row, sm.row[row].a, sm.row[row].bk, e, u, vv);
         return;
       }
     }
@@ -952,7 +974,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void k_kda(StepArgs A) {
   const int b = tile / A.P.H, h = tile - b * A.P.H;
   const long long slot = pool_slot<MODE>(A, b, h);
   if (slot < 0) return;
-  kda_tile<D, MODE>(A, b, slot, h, sm);
+  if (A.P.order) kda_tile<D, MODE, 1>(A, b, slot, h, sm);
+  else kda_tile<D, MODE, 0>(A, b, slot, h, sm);
 }
 
 // Debug decode: one workgroup per tile, same lane/row mapping, any head type.

@@ -20,6 +20,7 @@ enum Mode { FUSED = 0, READ = 1, WRITE = 2, ENCODE = 3 };
 // Device-resident plan tables (all arrays in device memory; per-row arrays are [H * d]).
 struct DevPlan {
   int H, D;                  // heads, d_k = d_v
+  int order;                 // 0: A = Diag(a)(I - beta k k^T); 1: A = (I - beta k k^T) Diag(a)
   long long bpr;             // bytes per request
   const long long* head_off; // [H] segment byte offset inside one request
   const int* head_type;      // [H]
@@ -61,8 +62,9 @@ struct StepArgs {
 hipError_t launch_step(int kind, Mode mode, const StepArgs& a, hipStream_t s);
 hipError_t launch_unpack(const DevPlan& P, const uint8_t* pool, int B, float* S, uint16_t* r,
                          uint16_t* c, int8_t* z, hipStream_t s);
-hipError_t launch_row_impact(int kind, int H, int D, int B, const float* q, const float* k,
-                             const float* alpha, const float* beta, double* acc, hipStream_t s);
+hipError_t launch_row_impact(int kind, int order, int H, int D, int B, const float* q,
+                             const float* k, const float* alpha, const float* beta, double* acc,
+                             hipStream_t s);
 hipError_t launch_spin(long long cycles, hipStream_t s);
 
 }  // namespace stepq

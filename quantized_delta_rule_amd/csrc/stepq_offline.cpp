@@ -40,22 +40,26 @@ int stepq_lifetime_weights(const double* l_u, int n, int H, double* L_out) {
 }
 
 int stepq_row_impact_accumulate(int n, int d, const float* q, const float* k, const float* a,
-                                const float* beta, double* acc) {
-  if (n < 0 || d < 1 || (n > 0 && (!q || !k || !a || !beta)) || !acc)
+                                const float* beta, int order, double* acc) {
+  if (n < 0 || d < 1 || (n > 0 && (!q || !k || !a || !beta)) || !acc ||
+      (order != STEPQ_ORDER_DELTA_FIRST && order != STEPQ_ORDER_DECAY_FIRST))
     return bad("row_impact_accumulate: bad arguments");
   std::vector<double> aq(d);
   for (int t = 0; t < n; t++) {
     const float* qt = q + (long long)t * d;
     const float* kt = k + (long long)t * d;
     const float* at = a + (long long)t * d;
-    double kaq = 0.0;
+    double kx = 0.0;  // k . (a*q), or k . q when the rows decay first
     for (int i = 0; i < d; i++) {
       aq[i] = (double)at[i] * (double)qt[i];
-      kaq += (double)kt[i] * aq[i];
+      kx += (double)kt[i] * (order == STEPQ_ORDER_DECAY_FIRST ? (double)qt[i] : aq[i]);
     }
-    const double s = (double)beta[t] * kaq;
+    const double s = (double)beta[t] * kx;
     for (int i = 0; i < d; i++) {
-      const double g = aq[i] - s * (double)kt[i];  // (Diag(a)(I - b k k^T))^T q
+      // g = A^T q:  Diag(a)(I - b k k^T) -> a*q - s k;  (I - b k k^T) Diag(a) -> a (q - s k)
+      const double g = order == STEPQ_ORDER_DECAY_FIRST
+                           ? (double)at[i] * ((double)qt[i] - s * (double)kt[i])
+                           : aq[i] - s * (double)kt[i];
       acc[i] += g * g;
     }
   }

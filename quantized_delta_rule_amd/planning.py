@@ -31,7 +31,7 @@ def omega(w: synth.Workload, layer: int, phase: str | None = None, steps: int | 
         a = synth.alpha_rows(w, x["alpha"])
         for h in range(w.H):
             stepq.row_impact_accumulate(x["q"][:, h], x["k"][:, h], a[:, h], x["beta"][:, h],
-                                        acc[h])
+                                        acc[h], order=w.order)
         n += w.B
     return (acc / n).astype(np.float32)
 
@@ -48,7 +48,7 @@ def omega_gpu(w: synth.Workload, layer: int, phase: str | None = None,
     kind = stepq.GDN if w.kind == "gdn" else stepq.KDA
     for s in range(steps):
         x = {k: torch.from_numpy(v).to(dev) for k, v in synth.step_inputs(w, layer, s, phase).items()}
-        stepq.row_impact_gpu(kind, x["q"], x["k"], x["alpha"], x["beta"], acc)
+        stepq.row_impact_gpu(kind, x["q"], x["k"], x["alpha"], x["beta"], acc, order=w.order)
     return (acc / (w.B * steps)).to(torch.float32).cpu().numpy().reshape(w.H, w.d)
 
 
@@ -68,7 +68,7 @@ def measured_distortion_gpu(w: synth.Workload, layer: int, omega_l, n_req: int =
     du = torch.zeros((H, d, len(w.choices)), dtype=torch.float64, device=dev)
     for ci, b in enumerate(w.choices):
         plan = stepq.Plan(kind, np.full((H, d), b, np.int8), np.zeros((H, d), np.uint8), omega_l,
-                          device=device)
+                          device=device, order=w.order)
         pool = plan.alloc_pool(n_req)
         for S in states:
             plan.encode(S, pool, n_req)

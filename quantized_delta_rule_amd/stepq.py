@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libstepq.so")
 
 GDN, KDA = 0, 1
 FUSED, SPLIT = 0, 1
+DELTA_FIRST, DECAY_FIRST = 0, 1   # gate order: A = Diag(a)(I - b k k^T) or (I - b k k^T) Diag(a)
 FLAG_NONFINITE, FLAG_SCALE_OVF, FLAG_PIVOT_OVF, FLAG_BAD_SLOT = 1, 2, 4, 8
 
 _lib = None
@@ -30,7 +31,7 @@ class _Desc(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("n_heads", ctypes.c_int), ("d_k", ctypes.c_int),
                 ("d_v", ctypes.c_int), ("bits", ctypes.c_void_p), ("pivot", ctypes.c_void_p),
                 ("omega", ctypes.c_void_p), ("mode", ctypes.c_int), ("max_batch", ctypes.c_int),
-                ("device", ctypes.c_int)]
+                ("device", ctypes.c_int), ("order", ctypes.c_int)]
 
 
 def lib() -> ctypes.CDLL:
@@ -59,8 +60,8 @@ def lib() -> ctypes.CDLL:
         "stepq_debug_side_delay": (i, [P, ctypes.c_longlong]),
         "stepq_last_error": (ctypes.c_char_p, []),
         "stepq_lifetime_weights": (i, [P, i, i, P]),
-        "stepq_row_impact_accumulate": (i, [i, i, P, P, P, P, P]),
-        "stepq_row_impact_gpu": (i, [i, i, i, i, P, P, P, P, P, P]),
+        "stepq_row_impact_accumulate": (i, [i, i, P, P, P, P, i, P]),
+        "stepq_row_impact_gpu": (i, [i, i, i, i, i, P, P, P, P, P, P]),
         "stepq_select_pivots": (i, [P, i, i, P]),
         "stepq_alloc_mcdp": (i, [P, i, P, i, ctypes.c_long, P, ctypes.POINTER(d)]),
         "stepq_alloc_lagrangian": (i, [P, P, P, i, P, i, d, i, P, ctypes.POINTER(d)]),
@@ -109,18 +110,19 @@ class Plan:
     """One layer's packed-state plan: widths, pivots and row impact per head (Method 1-2 of the
     STEPQuant digest), the derived packed layout, and (split mode) the side stream."""
 
-    def __init__(self, kind, bits, pivot, omega, mode=FUSED, max_batch=1, device=0):
+    def __init__(self, kind, bits, pivot, omega, mode=FUSED, max_batch=1, device=0,
+                 order=DELTA_FIRST):
         bits = _np(bits, np.int8)
         pivot = _np(pivot, np.uint8)
         omega = _np(omega, np.float32)
         if bits.ndim != 2 or pivot.shape != bits.shape or omega.shape != bits.shape:
             raise ValueError("bits, pivot and omega must all be [n_heads, d_k]")
-        self.kind, self.mode, self.device = int(kind), int(mode), int(device)
+        self.kind, self.mode, self.device, self.order = int(kind), int(mode), int(device), int(order)
         self.H, self.d = bits.shape
         self.max_batch = int(max_batch)
         self.bits, self.pivot, self.omega = bits, pivot, omega
         desc = _Desc(self.kind, self.H, self.d, self.d, bits.ctypes.data, pivot.ctypes.data,
-                     omega.ctypes.data, self.mode, self.max_batch, self.device)
+                     omega.ctypes.data, self.mode, self.max_batch, self.device, self.order)
         h = ctypes.c_void_p()
         _check(lib().stepq_plan_create(ctypes.byref(desc), ctypes.byref(h)), "plan_create")
         self._h = h
@@ -245,19 +247,19 @@ def lifetime_weights(l_u, H):
     return out
 
 
-def row_impact_accumulate(q, k, a, beta, acc):
+def row_impact_accumulate(q, k, a, beta, acc, order=DELTA_FIRST):
     q, k, a = _np(q, np.float32), _np(k, np.float32), _np(a, np.float32)
     beta = _np(beta, np.float32)
     n, d = q.shape
     assert k.shape == a.shape == (n, d) and beta.shape == (n,) and acc.shape == (d,)
     assert acc.dtype == np.float64 and acc.flags.c_contiguous
     _check(lib().stepq_row_impact_accumulate(n, d, q.ctypes.data, k.ctypes.data, a.ctypes.data,
-                                             beta.ctypes.data, acc.ctypes.data),
+                                             beta.ctypes.data, int(order), acc.ctypes.data),
            "row_impact_accumulate")
     return acc
 
 
-def row_impact_gpu(kind, q, k, alpha, beta, acc, stream=None):
+def row_impact_gpu(kind, q, k, alpha, beta, acc, stream=None, order=DELTA_FIRST):
     """acc [H*d] float64 (device) += sum over requests of g_i^2, g = A^T q, for one step of one
     layer: q, k [B, H, d], alpha [B, H] (GDN) or [B, H, d] (KDA), beta [B, H] (device fp32)."""
     import torch
@@ -270,7 +272,7 @@ def row_impact_gpu(kind, q, k, alpha, beta, acc, stream=None):
     args = [_dev_tensor(q, "q", f, B * H * d, dev), _dev_tensor(k, "k", f, B * H * d, dev),
             _dev_tensor(alpha, "alpha", f, na, dev), _dev_tensor(beta, "beta", f, B * H, dev),
             _dev_tensor(acc, "acc", torch.float64, H * d, dev)]
-    _check(lib().stepq_row_impact_gpu(int(kind), int(H), int(d), int(B), *args,
+    _check(lib().stepq_row_impact_gpu(int(kind), int(order), int(H), int(d), int(B), *args,
                                       _stream_ptr(stream)), "row_impact_gpu")
 
 

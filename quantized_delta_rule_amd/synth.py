@@ -46,6 +46,7 @@ class Workload:
     calib_steps: int = 0       # calibration steps for omega (KDA); 0 = use the warm-up
     horizon: int = 512         # H of the lifetime weight
     gates: str = "independent" # GDN gates: "independent" of l_u, or "lifetime" (log alpha ~ l_u)
+    order: int = 0             # gate order of A_t: 0 Diag(a)(I - b k k^T), 1 (I - b k k^T) Diag(a)
 
     @property
     def tiles_per_layer(self) -> int:

@@ -35,7 +35,8 @@ def omega_from_steps(w, layer, phase, steps):
         x = synth.step_inputs(w, layer, s, phase)
         a = synth.alpha_rows(w, x["alpha"])
         for h in range(w.H):
-            acc[h] += oracle.row_impact(x["q"][:, h], x["k"][:, h], a[:, h], x["beta"][:, h])
+            acc[h] += oracle.row_impact(x["q"][:, h], x["k"][:, h], a[:, h], x["beta"][:, h],
+                                        order=w.order)
     return (acc / steps).astype(np.float32)
 
 
@@ -58,7 +59,7 @@ def measured_distortion(w, omegas, n_req=8, samples=(32, 64)):
             v = np.stack([x["v"][:n_req].reshape(-1, d) for x in xs])
             a = np.stack([synth.alpha_rows(w, x["alpha"])[:n_req].reshape(-1, d) for x in xs])
             be = np.stack([x["beta"][:n_req].reshape(-1) for x in xs])
-            oracle.fp32_run(S, q, k, v, a, be)
+            oracle.fp32_run(S, q, k, v, a, be, order=w.order)
             for t in range(n_req * H):
                 h = t % H
                 for ci, b in enumerate(choices):
@@ -127,7 +128,7 @@ def warm_state(w, layer, threads=16):
     v = np.stack([x["v"].reshape(-1, d) for x in xs])
     a = np.stack([synth.alpha_rows(w, x["alpha"]).reshape(-1, d) for x in xs])
     be = np.stack([x["beta"].reshape(-1) for x in xs])
-    oracle.fp32_run(S, q, k, v, a, be, threads=threads)
+    oracle.fp32_run(S, q, k, v, a, be, threads=threads, order=w.order)
     return S
 
 
@@ -196,8 +197,8 @@ def run_layer(w, layer, bits, piv, om, steps, tiles=None, mode=0, S0=None, check
     d, H, B = w.d, w.H, w.B
     kind = stepq.GDN if w.kind == "gdn" else stepq.KDA
     if plan is None:
-        plan = stepq.Plan(kind, bits, piv, om, mode=mode, max_batch=B)
-    heads = [oracle.Head(bits[h], piv[h], om[h]) for h in range(H)]
+        plan = stepq.Plan(kind, bits, piv, om, mode=mode, max_batch=B, order=w.order)
+    heads = [oracle.Head(bits[h], piv[h], om[h], order=w.order) for h in range(H)]
     bpr = plan.bytes_per_request
     segs = [plan.head_segment(h) for h in range(H)]
     tiles = list(range(B * H)) if tiles is None else list(tiles)

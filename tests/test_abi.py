@@ -42,7 +42,7 @@ def _desc(sq, **kw):
 
 
 @pytest.mark.parametrize("case", ["bits", "omega_nan", "omega_neg", "gdn_mixed", "gdn_partial_pivot",
-                                  "d96", "pivot2"])
+                                  "d96", "pivot2", "order"])
 def test_invalid_plans_are_rejected(sq, case):
     H, d = 2, 128
     bits = np.full((H, d), 6, np.int8)
@@ -63,8 +63,9 @@ def test_invalid_plans_are_rejected(sq, case):
         bits, piv, om = bits[:, :96], piv[:, :96], om[:, :96]
     elif case == "pivot2":
         piv[0, 0] = 2
+    order = 2 if case == "order" else 0
     with pytest.raises(sq.StepqError) as ei:
-        sq.Plan(kind, bits, piv, om)
+        sq.Plan(kind, bits, piv, om, order=order)
     msg = str(ei.value)
     assert "(-1)" in msg or "(-2)" in msg, msg
 
@@ -85,7 +86,8 @@ def test_lifetime_weights_match_oracle(sq, orc):
     assert np.allclose(sq.lifetime_weights(l, 512), orc.lifetime_weight(l, 512), rtol=1e-12)
 
 
-def test_row_impact_matches_oracle(sq, orc):
+@pytest.mark.parametrize("order", [0, 1])
+def test_row_impact_matches_oracle(sq, orc, order):
     g = np.random.default_rng(1)
     n, d = 64, 128
     q = g.standard_normal((n, d)).astype(np.float32)
@@ -93,8 +95,8 @@ def test_row_impact_matches_oracle(sq, orc):
     a = g.uniform(0.8, 1, (n, d)).astype(np.float32)
     b = g.uniform(0, 1, n).astype(np.float32)
     acc = np.zeros(d)
-    sq.row_impact_accumulate(q, k, a, b, acc)
-    assert np.allclose(acc / n, orc.row_impact(q, k, a, b), rtol=1e-10)
+    sq.row_impact_accumulate(q, k, a, b, acc, order=order)
+    assert np.allclose(acc / n, orc.row_impact(q, k, a, b, order=order), rtol=1e-10)
 
 
 def test_pivots_match_oracle(sq, orc):

@@ -23,11 +23,12 @@ def gpu():
     return torch
 
 
+@pytest.mark.parametrize("order", [0, 1])
 @pytest.mark.parametrize("kind,d", [("gdn", 128), ("kda", 64), ("kda", 128), ("gdn", 64)])
-def test_row_impact_gpu_matches_oracle(gpu, kind, d):
+def test_row_impact_gpu_matches_oracle(gpu, kind, d, order):
     from quantized_delta_rule_amd import planning
     base = synth.WORKLOADS[2 if kind == "gdn" else 4]
-    w = dataclasses.replace(base, B=5, H=3, d=d, calib_steps=0, warmup=4)
+    w = dataclasses.replace(base, B=5, H=3, d=d, calib_steps=0, warmup=4, order=order)
     om_gpu = planning.omega_gpu(w, 0)
     om_orc = P.omega_from_steps(w, 0, "warmup", w.warmup)
     om_host = planning.omega(w, 0)

@@ -89,3 +89,23 @@ def test_empty_batch_is_a_no_op(torch_gpu):
     plan.step(pool, 0, z, z, z, z, z, z)
     torch.cuda.synchronize()
     assert int(pool.sum()) == 0
+
+@pytest.mark.parametrize("kind,d,mode", [("kda", 128, 0), ("kda", 64, 0), ("kda", 128, 1),
+                                         ("gdn", 128, 0), ("gdn", 64, 1)])
+def test_decay_first_gate_order(torch_gpu, kind, d, mode):
+    """Plan order 1, A = (I - beta k k^T) Diag(a): every tile and step against the oracle's
+    decay-first step, fused and split, KDA with mixed rows and pivots and GDN with each width."""
+    if kind == "kda":
+        w = dataclasses.replace(_small(700 + d + mode, kind="kda", d=d, H=3), order=1)
+        g = np.random.default_rng(d + mode)
+        bits = g.choice([2, 4, 6, 8], size=(w.H, d)).astype(np.int8)
+        piv = np.zeros((w.H, d), np.uint8)
+        piv[1, g.choice(d, 5, replace=False)] = 1
+        om = P.omega_from_steps(w, 0, "warmup", w.warmup)
+    else:
+        w = dataclasses.replace(_small(710 + d + mode, d=d, H=5, fixed_bits=(2, 4, 6, 8, 0)),
+                                order=1)
+        bits, piv, om = (a[0] for a in P.oracle_plan(w))
+    P.log(f"[parity] decay-first {kind} d={d} mode={mode}")
+    tr, plan, _ = P.run_layer(w, 0, bits, piv, om, w.steps, mode=mode)
+    assert plan.status() == 0
