@@ -2,6 +2,7 @@
 // launches and stream ordering.  The ABI is declared (and each call documented) in stepq.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -195,6 +196,18 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
     for (int i = 0; i < D; i++) den[(long long)h * D + i] = mean > 0.0f ? 1.0f + ho[i] / mean : 1.0f;
   }
 
+  // Dispatch order of the heads: the tiles with the most vector work first, the cheapest last
+  // (4- and 2-bit, then 6-bit, then 8-bit heads, FP16 pivot heads at the end), so that the
+  // launch ends on short tiles.  Ties keep the head index order.
+  std::vector<int> head_order(H);
+  for (int h = 0; h < H; h++) head_order[h] = h;
+  auto rank = [&](int h) {
+    const int t = head_type[h];
+    return t == kHeadPivot ? 0 : t == 8 ? 1 : t == 6 ? 2 : 3;
+  };
+  std::stable_sort(head_order.begin(), head_order.end(),
+                   [&](int x, int y) { return rank(x) > rank(y); });
+
   auto* p = new (std::nothrow) stepq_plan();
   if (!p) return fail(STEPQ_ERR_OOM, "host allocation failed");
   p->kind = d->kind;
@@ -224,6 +237,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   };
   const size_t i_hoff = add(head_off.data(), H * sizeof(long long));
   const size_t i_type = add(head_type.data(), H * sizeof(int));
+  const size_t i_hord = add(head_order.data(), H * sizeof(int));
   const size_t i_opiv = add(off_piv.data(), H * sizeof(int));
   const size_t i_or = add(off_r.data(), H * sizeof(int));
   const size_t i_oc = add(off_c.data(), H * sizeof(int));
@@ -257,6 +271,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   dp.bpr = p->bpr;
   dp.head_off = (const long long*)at(i_hoff);
   dp.head_type = (const int*)at(i_type);
+  dp.head_order = (const int*)at(i_hord);
   dp.off_piv = (const int*)at(i_opiv);
   dp.off_r = (const int*)at(i_or);
   dp.off_c = (const int*)at(i_oc);

@@ -81,7 +81,7 @@ __device__ __forceinline__ float rcp0(float x) { return x == 0.0f ? 0.0f : 1.0f 
 __device__ __forceinline__ float rcp16(float x) {
   const float y0 = __builtin_amdgcn_rcpf(x);
   const float r = __builtin_fmaf(y0, __builtin_fmaf(-x, y0, 1.0f), y0);
-  return __builtin_amdgcn_class(x, 0x264) ? 0.0f : r;  // class bits: -inf, -0, +0, +inf
+  return __builtin_amdgcn_classf(x, 0x264) ? 0.0f : r;  // class bits: -inf, -0, +0, +inf
 }
 
 __device__ __forceinline__ bool is_inf16(uint16_t h) { return (h & 0x7FFFu) == 0x7C00u; }
@@ -951,11 +951,13 @@ __device__ __forceinline__ long long pool_slot(const StepArgs& A, int b, int h) 
   return valid ? s : -1;
 }
 
+// Workgroup j runs head head_order[j / B] of request j % B: heads are dispatched in the plan's
+// order (longest tiles first, FP16 pivot heads last), which shortens the launch's ragged end.
 template <int D, int MODE>
 __global__ __launch_bounds__(Geo<D>::NT, 4) void k_gdn(StepArgs A) {
   __shared__ Smem<D, false> sm;
-  const int tile = blockIdx.x;
-  const int b = tile / A.P.H, h = tile - b * A.P.H;
+  const int hs = blockIdx.x / A.B, b = blockIdx.x - hs * A.B;
+  const int h = A.P.head_order[hs];
   const long long slot = pool_slot<MODE>(A, b, h);
   if (slot < 0) return;
   switch (A.P.head_type[h]) {

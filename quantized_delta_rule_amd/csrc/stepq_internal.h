@@ -24,6 +24,7 @@ struct DevPlan {
   long long bpr;             // bytes per request
   const long long* head_off; // [H] segment byte offset inside one request
   const int* head_type;      // [H]
+  const int* head_order;     // [H] dispatch order of the heads (GDN fused/split/encode kernels)
   const int* off_piv;        // [H] pivot block offset inside the segment
   const int* off_r;          // [H] row-factor block offset
   const int* off_c;          // [H] column-factor block offset
