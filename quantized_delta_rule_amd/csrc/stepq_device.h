@@ -423,7 +423,7 @@ __device__ __forceinline__ void col_factor(const float* num, const float* sq, co
     const float c1 = sq[g] > 0.0f ? num[g] / sq[g] : c0[g];
     const uint16_t ch = f2h(c1);
     if (is_inf16(ch)) fl |= kFlagScaleOvf;
-    if (w == 0) cblk[G * lane + g] = ch;
+    if (w == 0 && cblk) cblk[G * lane + g] = ch;
     ic[g] = rcp16(h2f(ch));
   });
 }
@@ -743,9 +743,10 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
   uint8_t* seg = A.pool + slot * A.P.bpr + A.P.head_off[h];
   uint32_t* words = reinterpret_cast<uint32_t*>(seg);
   uint16_t* pblk = reinterpret_cast<uint16_t*>(seg + A.P.off_piv[h]);
-  uint16_t* rblk = reinterpret_cast<uint16_t*>(seg + A.P.off_r[h]);
-  uint16_t* cblk = reinterpret_cast<uint16_t*>(seg + A.P.off_c[h]);
   const int nwords = A.P.words[h];
+  // a head whose rows are all FP16 pivots stores no row or column factors
+  uint16_t* rblk = nwords > 0 ? reinterpret_cast<uint16_t*>(seg + A.P.off_r[h]) : nullptr;
+  uint16_t* cblk = nwords > 0 ? reinterpret_cast<uint16_t*>(seg + A.P.off_c[h]) : nullptr;
   const int* bitsv = A.P.bits + h * D;
   const int* posv = A.P.rowpos + h * D;
   const int* pidv = A.P.pividx + h * D;
@@ -762,7 +763,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     u32x4* l4 = reinterpret_cast<u32x4*>(sm.kc.code);
     for (int x = tid; x < n4; x += NT) l4[x] = __builtin_nontemporal_load(&g4[x]);
     if (tid < 16) l4[n4 + tid] = u32x4{0u, 0u, 0u, 0u};  // window over the last word
-    sfor<G>([&](auto gg) { cc[CI(gg)] = h2f(cblk[G * lane + CI(gg)]); });
+    sfor<G>([&](auto gg) { cc[CI(gg)] = cblk ? h2f(cblk[G * lane + CI(gg)]) : 0.0f; });
   }
   load_inputs<D, MODE, true, kUV>(A, sm, tile, lane, row, MODE != ENCODE ? rblk : nullptr, alpha, vv,
                              e, u);
@@ -991,7 +992,7 @@ __global__ __launch_bounds__(D) void k_unpack(DevPlan P, const uint8_t* pool, fl
   const uint8_t* seg = pool + (long long)b * P.bpr + P.head_off[h];
   const uint32_t* words = reinterpret_cast<const uint32_t*>(seg);
   const uint16_t* pblk = reinterpret_cast<const uint16_t*>(seg + P.off_piv[h]);
-  const bool allpiv = P.head_type[h] == kHeadPivot;
+  const bool allpiv = P.words[h] == 0;  // every row an FP16 pivot: no factor blocks
   const uint16_t* rblk = reinterpret_cast<const uint16_t*>(seg + P.off_r[h]);
   const uint16_t* cblk = reinterpret_cast<const uint16_t*>(seg + P.off_c[h]);
   if (rout) rout[(long long)tile * D + trow] = allpiv ? 0 : rblk[trow];

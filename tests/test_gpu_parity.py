@@ -109,3 +109,83 @@ def test_decay_first_gate_order(torch_gpu, kind, d, mode):
     P.log(f"[parity] decay-first {kind} d={d} mode={mode}")
     tr, plan, _ = P.run_layer(w, 0, bits, piv, om, w.steps, mode=mode)
     assert plan.status() == 0
+
+
+@pytest.mark.parametrize("d,mode", [(128, 0), (64, 1)])
+def test_kda_head_with_every_row_a_pivot(torch_gpu, d, mode):
+    """A KDA head whose rows are all FP16 pivots stores no factor blocks; its neighbours must be
+    untouched and every tile must match the oracle (fused and split), and the debug decode
+    must return the stored binary16 values."""
+    torch = torch_gpu
+    from quantized_delta_rule_amd import stepq
+    w = _small(800 + d + mode, kind="kda", d=d, H=3)
+    g = np.random.default_rng(d)
+    bits = g.choice([2, 4, 6, 8], size=(w.H, d)).astype(np.int8)
+    piv = np.zeros((w.H, d), np.uint8)
+    piv[1, :] = 1                      # head 1: every row a pivot
+    piv[2, [0, d - 1]] = 1
+    om = P.omega_from_steps(w, 0, "warmup", w.warmup)
+    P.log(f"[parity] KDA all-pivot head d={d} mode={mode}")
+    tr, plan, pool = P.run_layer(w, 0, bits, piv, om, w.steps, mode=mode)
+    assert plan.status() == 0
+    off, n = plan.head_segment(1)
+    assert n == 2 * d * d              # the raw binary16 tile only
+    Sg, rg, cg, zg = (x.cpu().numpy() for x in plan.unpack(pool, w.B))
+    host = pool.cpu().numpy()
+    import oracle
+    for b in range(w.B):
+        seg = host[b * plan.bytes_per_request + off:][:n]
+        So, _, _, _ = oracle.Head(bits[1], piv[1], om[1]).unpack(seg)
+        assert np.array_equal(Sg[b, 1].view(np.uint32), So.view(np.uint32))
+        assert not rg[b, 1].any() and not cg[b, 1].any() and not zg[b, 1].any()
+
+
+def test_status_flags_match_oracle(torch_gpu):
+    """Binary16 overflow of a row/column factor, of an FP16 pivot entry, and a non-finite
+    updated state raise the same status bits on the GPU as in the oracle."""
+    torch = torch_gpu
+    import oracle
+    from quantized_delta_rule_amd import stepq
+    dev = torch.device("cuda:0")
+    w = _small(901, d=128, B=2, H=2, fixed_bits=(6, 0))
+    bits, piv, om = (a[0] for a in P.oracle_plan(w))
+    heads = [oracle.Head(bits[h], piv[h], om[h]) for h in range(w.H)]
+    plan = stepq.Plan(stepq.GDN, bits, piv, om)
+    S0 = P.warm_state(w, 0)
+    S0[0] *= 1e7                       # quantized head 0 of request 0: its factors overflow
+    S0[3] *= 1e7                       # pivot head 1 of request 1: its entries overflow
+    pool = plan.alloc_pool(w.B)
+    plan.encode(torch.from_numpy(S0).to(dev), pool, w.B)
+    want = 0
+    for t in range(w.B * w.H):
+        _, _, fl = heads[t % w.H].encode(S0[t], want_pre=True)
+        want |= fl
+    got = plan.status(reset=True)
+    P.log(f"[parity] encode flags gpu {got} oracle {want}")
+    assert want == stepq.FLAG_SCALE_OVF | stepq.FLAG_PIVOT_OVF
+    assert got == want
+    # a NaN in v makes the updated state non-finite
+    S1 = P.warm_state(w, 0)
+    plan.encode(torch.from_numpy(S1).to(dev), pool, w.B)
+    torch.cuda.synchronize()
+    segs = [pool.cpu().numpy()[b * plan.bytes_per_request:][:plan.bytes_per_request].copy()
+            for b in range(w.B)]
+    assert plan.status(reset=True) == 0
+    x = synth.step_inputs(w, 0, 0)
+    x["v"][1, 0, 5] = np.nan
+    gx = {k: torch.from_numpy(v).to(dev) for k, v in x.items()}
+    out = torch.empty((w.B, w.H, w.d), device=dev)
+    plan.step(pool, w.B, gx["q"], gx["k"], gx["v"], gx["alpha"], gx["beta"], out)
+    want = 0
+    a_rows = synth.alpha_rows(w, x["alpha"])
+    for t in range(w.B * w.H):
+        b, h = divmod(t, w.H)
+        off, n = plan.head_segment(h)
+        seg = segs[b][off:off + n].copy()
+        _, _, _, fl = heads[h].step(seg, x["q"][b, h], x["k"][b, h], x["v"][b, h],
+                                    a_rows[b, h], x["beta"][b, h], want_state=True)
+        want |= fl
+    got = plan.status(reset=True)
+    P.log(f"[parity] step flags gpu {got} oracle {want}")
+    assert want & stepq.FLAG_NONFINITE
+    assert got == want
