@@ -101,13 +101,19 @@ def cpu_baseline(w, plan_arrays, S_tiles, budget_s, threads):
                       f"{done} tile-steps in {dt:.1f} s"}
 
 
+# Pool replicas rotated per timed step (one-layer workloads): enough that the replicas together
+# exceed twice the 256 MB Infinity Cache, so the packed state streams from HBM.
+REPLICAS = {1: 12, 2: 12, 3: 10, 4: 20, 6: 12}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=600)
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--replicas", type=int, default=12)
+    ap.add_argument("--replicas", type=int, default=None,
+                    help="pool replicas rotated per step (one-layer workloads)")
     ap.add_argument("--inputs", type=int, default=4, help="distinct input sets per replica")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -126,88 +132,114 @@ def main():
 
     dev = torch.device("cuda:0")
     w = synth.WORKLOADS[args.workload]
-    if w.layers != 1 or w.split:
-        raise SystemExit("bench.py times single-layer fused workloads")
     print(f"[bench] workload {w.wid} {w.name}: planning", file=sys.stderr, flush=True)
     bits, piv, om = planning.plan_arrays(w)
     kind = stepq.GDN if w.kind == "gdn" else stepq.KDA
-    plan = stepq.Plan(kind, bits[0], piv[0], om[0])
-    alg_bytes = planning.algorithmic_bytes(w, plan)
-    R = args.replicas
+    mode = stepq.SPLIT if w.split else stepq.FUSED
+    multi = w.layers > 1
+    # one plan per layer; a one-layer workload steps R independent replicas of its pool in turn
+    plans = [stepq.Plan(kind, bits[l], piv[l], om[l], mode=mode, max_batch=w.B, order=w.order)
+             for l in range(w.layers)]
+    R = 1 if multi else (args.replicas or REPLICAS.get(w.wid, 12))
+    units = [(plans[l], l) for l in range(w.layers)] if multi else [(plans[0], r) for r in range(R)]
+    alg_bytes = sum(planning.algorithmic_bytes(w, p) for p in plans)
+    alg_ops = sum(planning.algorithmic_ops(w, p) for p in plans)
     pools, inputs, S_sample = [], [], {}
-    for r in range(R):
-        S0 = warm_state(w, r, dev)
+    for i, (plan, seed) in enumerate(units):
+        S0 = warm_state(w, seed, dev)
         pool = plan.alloc_pool(w.B)
         plan.encode(S0, pool, w.B)
-        if r == 0 and not args.no_cpu:
+        if i == 0 and not args.no_cpu:
             pick = [b * w.H + h for b, h in zip(range(0, w.B, max(1, w.B // w.H)), range(w.H))]
             S_sample = {t: S0[t].cpu().numpy() for t in pick}
         del S0
         pools.append(pool)
         sets = []
         for j in range(args.inputs):
-            x = synth.step_inputs(w, r, j, "decode")
+            x = synth.step_inputs(w, seed, j, "decode")
             sets.append({k: torch.from_numpy(v).to(dev) for k, v in x.items()})
         inputs.append(sets)
     torch.cuda.synchronize()
-    print(f"[bench] {R} replicas x {plan.bytes_per_request * w.B / 2**20:.1f} MiB pool "
-          f"({plan.bits_per_value:.3f} bits/value), timing", file=sys.stderr, flush=True)
+    pool_mib = sum(p.bytes_per_request for p in plans) * w.B / 2 ** 20
+    print(f"[bench] {len(units)} {'layers' if multi else 'replicas'} x "
+          f"{plans[0].bytes_per_request * w.B / 2**20:.1f} MiB pool "
+          f"({plans[0].bits_per_value:.3f} bits/value), timing", file=sys.stderr, flush=True)
 
     out = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device=dev)
     L = stepq.lib()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     P = ctypes.c_void_p
-    calls = []
-    for r in range(R):
-        for j in range(args.inputs):
-            x = inputs[r][j]
-            calls.append((plan._h, P(pools[r].data_ptr()), w.B, P(x["q"].data_ptr()),
-                          P(x["k"].data_ptr()), P(x["v"].data_ptr()), P(x["alpha"].data_ptr()),
-                          P(x["beta"].data_ptr()), P(out.data_ptr()), stream))
-    # order: replica-major rotation so consecutive steps touch different pools
-    order = [calls[(i % R) * args.inputs + (i // R) % args.inputs] for i in range(len(calls))]
+
+    def call(u, j):
+        plan, x = units[u][0], inputs[u][j]
+        return (plan._h, P(pools[u].data_ptr()), w.B, P(x["q"].data_ptr()),
+                P(x["k"].data_ptr()), P(x["v"].data_ptr()), P(x["alpha"].data_ptr()),
+                P(x["beta"].data_ptr()), P(out.data_ptr()), stream)
+
+    # a step: every layer once (multi-layer workloads), or one replica in turn, replica-major
+    # rotation so consecutive steps touch different pools
+    if multi:
+        steps = [[call(u, j) for u in range(len(units))] for j in range(args.inputs)]
+    else:
+        flat = [call(u, j) for u in range(R) for j in range(args.inputs)]
+        steps = [[flat[(i % R) * args.inputs + (i // R) % args.inputs]] for i in range(len(flat))]
+    launches = len(steps[0])
     step_fn = L.stepq_decode_step
 
+    def run(i):
+        for c in steps[i % len(steps)]:
+            step_fn(*c)
+
+    def drain():
+        torch.cuda.synchronize()
+        for p in plans:
+            p.sync()
+
     for i in range(args.warmup):
-        rc = step_fn(*order[i % len(order)])
-        if rc:
-            raise RuntimeError(L.stepq_last_error().decode())
-    torch.cuda.synchronize()
-    # timed region: K back-to-back launches on the launch stream, one event pair around them
-    # (an event pair per launch would add its own overhead to every step)
+        for c in steps[i % len(steps)]:
+            if step_fn(*c):
+                raise RuntimeError(L.stepq_last_error().decode())
+    drain()
+    # timed region: K steps back to back on the launch stream, one event pair around them (an
+    # event pair per launch would add its own overhead to every step); split-mode refits run on
+    # the plans' side streams and are included by the host clock
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for i in range(args.steps):
-        step_fn(*order[i % len(order)])
+        run(i)
     ev1.record()
-    torch.cuda.synchronize()
+    drain()
     wall = time.perf_counter() - t0
-    avg_k = ev0.elapsed_time(ev1) / args.steps
-    if plan.status() != 0:
+    avg_k = ev0.elapsed_time(ev1) / (args.steps * launches)
+    if any(p.status() != 0 for p in plans):
         raise RuntimeError("status flags raised during the benchmark")
+    ms_per_step = wall * 1e3 / args.steps
+    # the kernel time a step takes: the launch stream's events (fused), or the host clock when
+    # a side stream carries part of the work (split)
+    step_ms = ms_per_step if w.split else avg_k * launches
 
-    # spread over launches (outside the timed region): each launch between its own event pair,
-    # so these figures include that pair's overhead
-    nspread = min(100, args.steps)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(nspread)]
-    for i in range(nspread):
-        ev[i][0].record()
-        step_fn(*order[i % len(order)])
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    k_ms = np.array([a.elapsed_time(b) for a, b in ev])
-
-    # cache-hot reference: one pool stepped repeatedly (labelled, not the headline)
-    h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    h0.record()
-    for _ in range(50):
-        step_fn(*order[0])
-    h1.record()
-    torch.cuda.synchronize()
-    hot_ms = h0.elapsed_time(h1) / 50
+    k_ms, hot_ms = None, None
+    if not multi:
+        # spread over launches (outside the timed region): each launch between its own event
+        # pair, so these figures include that pair's overhead
+        nspread = min(100, args.steps)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(nspread)]
+        for i in range(nspread):
+            ev[i][0].record()
+            run(i)
+            ev[i][1].record()
+        drain()
+        k_ms = np.array([a.elapsed_time(b) for a, b in ev])
+        # cache-hot reference: one pool stepped repeatedly (labelled, not the headline)
+        h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        h0.record()
+        for _ in range(50):
+            step_fn(*steps[0][0])
+        h1.record()
+        drain()
+        hot_ms = h0.elapsed_time(h1) / 50
 
     if args.copy_calib:
         src = torch.empty(2 ** 28, dtype=torch.float32, device=dev)
@@ -216,16 +248,42 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    ms_per_step = wall * 1e3 / args.steps
     heads = w.B * w.H * w.layers
-    achieved = alg_bytes / (avg_k * 1e-3) / 1e9
-    alg_ops = planning.algorithmic_ops(w, plan)
-    achieved_ops = alg_ops / (avg_k * 1e-3) / 1e12
+    achieved = alg_bytes / (step_ms * 1e-3) / 1e9
+    achieved_ops = alg_ops / (step_ms * 1e-3) / 1e12
+    kname = ("k_gdn" if w.kind == "gdn" else "k_kda") + f"<{w.d}, " + \
+        ("READ> + WRITE (side stream)" if w.split else "FUSED>")
     traffic = None
     if os.path.exists(COUNTERS):
         c = json.load(open(COUNTERS))
-        if c.get("kernel_sha") == kernel_sha():
+        if c.get("kernel_sha") == kernel_sha() and c.get("workload") == w.name:
             traffic = c["hbm_bytes_per_launch"]
+    unit_desc = (f"MC-DP map {w.choices}" if w.alloc == "mcdp" else
+                 f"Lagrangian row map {w.choices}" if w.alloc == "lagrangian" else
+                 f"fixed head widths {w.fixed_bits}")
+    config = {
+        "workload": f"{w.name}: {w.B} requests x {w.layers} layer(s) x {w.H} "
+                    f"{w.kind.upper()} heads, d_k=d_v={w.d}, nominal {w.nominal}-bit {unit_desc}"
+                    f", {w.n_pivots} FP16 pivot unit(s), "
+                    + (f"{w.layers} layers back to back per step, refit and writeback on a side "
+                       f"stream" if multi else f"{R} rotating pool replicas"),
+        "bits_per_value": round(plans[0].bits_per_value, 4),
+        "pool_mib_per_replica": round(pool_mib, 2),
+        "algorithmic_bytes_per_step": alg_bytes,
+        "kernel_ms_mean": avg_k,
+        "launches_per_step": launches,
+        "hbm": {"achieved_GBps": achieved, "peak_GBps": PEAK_HBM_GBS,
+                "frac": achieved / PEAK_HBM_GBS},
+        "algorithmic_ops_per_step": alg_ops,
+    }
+    if k_ms is not None:
+        config["event_bracketed_launch_ms_p10_p50_p90"] = [float(np.percentile(k_ms, p))
+                                                           for p in (10, 50, 90)]
+        config["cache_hot_single_pool_kernel_ms"] = hot_ms
+        config["cache_hot_single_pool_GBps"] = alg_bytes / (hot_ms * 1e-3) / 1e9
+    if w.split:
+        config["split_code_reread_bytes_per_step"] = sum(
+            planning.code_bytes(w, p) for p in plans)
     res = {
         "metric": METRIC,
         "value": heads / (ms_per_step * 1e-3),
@@ -239,27 +297,12 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {
-            "workload": f"{w.name}: {w.B} requests x {w.H} GDN heads, d_k=d_v={w.d}, nominal "
-                        f"{w.nominal}-bit MC-DP map {w.choices} + {w.n_pivots} FP16 pivot head, "
-                        f"{R} rotating pool replicas",
-            "bits_per_value": round(plan.bits_per_value, 4),
-            "pool_mib_per_replica": round(plan.bytes_per_request * w.B / 2 ** 20, 2),
-            "algorithmic_bytes_per_step": alg_bytes,
-            "kernel_ms_mean": avg_k,
-            "event_bracketed_launch_ms_p10_p50_p90": [float(np.percentile(k_ms, p))
-                                                      for p in (10, 50, 90)],
-            "cache_hot_single_pool_kernel_ms": hot_ms,
-            "cache_hot_single_pool_GBps": alg_bytes / (hot_ms * 1e-3) / 1e9,
-            "hbm": {"achieved_GBps": achieved, "peak_GBps": PEAK_HBM_GBS,
-                    "frac": achieved / PEAK_HBM_GBS},
-            "algorithmic_ops_per_step": alg_ops,
-        },
-        # the kernel is bound by vector-ALU issue (the cache-hot pool is barely faster than the
-        # HBM-streaming one); traffic is the counter-measured HBM bytes per launch
+        "config": config,
+        # the kernel is bound by vector-ALU issue (the cache-hot pool is only ~15% faster than
+        # the HBM-streaming one); traffic is the counter-measured HBM bytes per launch
         "roofline": {"bound": "alu", "achieved": achieved_ops, "peak": PEAK_ALU_TOPS,
                      "unit": "TOP/s", "frac": achieved_ops / PEAK_ALU_TOPS, "traffic": traffic,
-                     "kernel": "k_gdn<128, FUSED>", "kernel_sha": kernel_sha()},
+                     "kernel": kname, "kernel_sha": kernel_sha()},
     }
     if not args.no_cpu and S_sample:
         threads = max(1, min(16, os.cpu_count() or 1))

@@ -145,7 +145,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   std::vector<int> head_type(H), off_piv(H), off_r(H), off_c(H), words(H);
   std::vector<long long> head_off(H), head_bytes(H);
   std::vector<float> den(nrow), qmax(nrow), iq(nrow), omega(d->omega, d->omega + nrow);
-  std::vector<int> bits(nrow), rowpos(nrow), pividx(nrow);
+  std::vector<int> bits(nrow), rowpos(nrow), pividx(nrow), rowmeta(nrow);
   long long off = 0;
   for (int h = 0; h < H; h++) {
     const int8_t* hb = d->bits + (long long)h * D;
@@ -156,6 +156,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
     for (int i = 0; i < D; i++) {
       const long long r = (long long)h * D + i;
       if (hp[i]) {
+        rowmeta[r] = (int)(0x80000000u | (unsigned)npiv);
         pividx[r] = npiv++;
         rowpos[r] = -1;
         bits[r] = 0;
@@ -164,6 +165,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
       } else {
         pividx[r] = -1;
         rowpos[r] = (int)lane_bits;
+        rowmeta[r] = (int)lane_bits | (hb[i] << 16);
         bits[r] = hb[i];
         lane_bits += (long long)G * hb[i];
         qmax[r] = (float)((1 << (hb[i] - 1)) - 1);
@@ -249,6 +251,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   const size_t i_bits = add(bits.data(), nrow * sizeof(int));
   const size_t i_pos = add(rowpos.data(), nrow * sizeof(int));
   const size_t i_pid = add(pividx.data(), nrow * sizeof(int));
+  const size_t i_meta = add(rowmeta.data(), nrow * sizeof(int));
   const unsigned zero = 0;
   const size_t i_st = add(&zero, sizeof(unsigned));
   hipError_t e = hipMalloc(&p->dtab, total);
@@ -283,6 +286,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   dp.bits = (const int*)at(i_bits);
   dp.rowpos = (const int*)at(i_pos);
   dp.pividx = (const int*)at(i_pid);
+  dp.rowmeta = (const int*)at(i_meta);
   dp.status = (unsigned*)at(i_st);
   p->status = dp.status;
 

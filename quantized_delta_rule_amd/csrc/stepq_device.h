@@ -131,15 +131,24 @@ struct Row<false> {
 };
 template <>
 struct Row<true> {
-  float kr, ar, a, bk, q, ir, W, iq;  // ... and the row's own gate a and 1/qmax
+  float kr, ar, a, bk, ir, W;  // as above without q (kept in the staging area), plus the gate a
+  int meta;                    // packed width, stream position or pivot index (row_meta)
 };
 
-template <int D, bool KDA>
-struct RowsKda {  // per-row qmax of mixed-width tiles
-  float qm[D];
-};
-template <int D>
-struct RowsKda<D, false> {};
+// Per-row layout metadata of mixed-width tiles, packed by the plan into one int: a pivot row is
+// 0x80000000 | (its index in the pivot block); a quantized row is its stream bit position |
+// (width << 16).  Read once per row and phase as a wave-uniform scalar.
+__device__ __forceinline__ bool meta_pivot(int m) { return m < 0; }
+__device__ __forceinline__ int meta_low(int m) { return m & 0xFFFF; }  // pivot index / position
+__device__ __forceinline__ int meta_bits(int m) { return (m >> 16) & 15; }
+// qmax = 2^(b-1) - 1 and 1/qmax (binary32, correctly rounded) of a row by its packed metadata,
+// 0 for a pivot row: tables in constant memory, read with the wave-uniform index through the
+// scalar cache (no per-row selects in vector registers).
+__constant__ float kQmaxTab[5] = {0.0f, 1.0f, 7.0f, 31.0f, 127.0f};
+__constant__ float kIqmaxTab[5] = {0.0f, 1.0f, 1.0f / 7.0f, 1.0f / 31.0f, 1.0f / 127.0f};
+__device__ __forceinline__ int meta_width_class(int m) { return m < 0 ? 0 : ((m >> 16) & 15) >> 1; }
+__device__ __forceinline__ float qmax_of_meta(int m) { return kQmaxTab[meta_width_class(m)]; }
+__device__ __forceinline__ float iqmax_of_meta(int m) { return kIqmaxTab[meta_width_class(m)]; }
 template <int D, bool KDA>
 struct CodeKda {  // code block staging of mixed-width tiles
   uint32_t code[(2 * D * 8 / 32 + 1) * 64];
@@ -147,22 +156,28 @@ struct CodeKda {  // code block staging of mixed-width tiles
 template <int D>
 struct CodeKda<D, false> {};
 
-// GDN tiles need at most 40 KB, so four workgroups fit in a CU's 160 KB: their 1/qmax and qmax
-// are compile-time constants, and the column maxima pass through each wave's own (by then dead)
-// transpose section, so two cross-wave slots suffice.
+// Both tile kinds fit in 40 KB, so four workgroups fit in a CU's 160 KB.  Only two cross-wave
+// slots: GDN column maxima pass through each wave's own (by then dead) transpose section; KDA
+// keeps them, and the rows' q, in the transpose area just past its code staging block (q is
+// dead after the readout barrier, before the transpose; the maxima come after it).
 template <int D, bool KDA>
 struct Smem {
   static constexpr int NW = Geo<D>::NW;
   static constexpr bool kKDA = KDA;
-  static constexpr int NSLOT = KDA ? 3 : 2;
+  static constexpr int NSLOT = 2;
   Row<KDA> row[D];
-  [[no_unique_address]] RowsKda<D, KDA> kr;
   float red[NSLOT][NW][D];
   union {
     float absT[NW][32][65];  // [wave][row][lane], +1 pad: conflict-free
     CodeKda<D, KDA> kc;      // used only before and after the transpose
   };
+  // KDA: column-maximum slots [NW][D] and the rows' q [D], after the code staging block
+  static constexpr int kKdaMax = KDA ? (int)(sizeof(CodeKda<D, KDA>) / sizeof(float)) : 0;
+  static constexpr int kKdaQ = kKdaMax + NW * D;
+  static_assert(!KDA || kKdaQ + D <= NW * 32 * 65, "KDA staging overflows the transpose area");
 };
+static_assert(sizeof(Smem<128, false>) <= 40960 && sizeof(Smem<128, true>) <= 40960,
+              "four workgroups per CU need at most 40 KB of LDS each");
 
 // An integer the optimizer cannot see through: each array's row base below gets its own copy,
 // so the array's address stays in its own VGPR and each access uses the instruction's small
@@ -184,12 +199,14 @@ __device__ __forceinline__ T* lds_pin(SM& sm, T* p) {
 template <typename SM>
 struct Rows {
   const Row<SM::kKDA>* r;
-  const float* qm;
   __device__ __forceinline__ Rows(const SM& sm) {
     const int base = (threadIdx.x >> 6) * 32;
     r = &sm.row[opaque(base)];
-    qm = nullptr;
-    if constexpr (SM::kKDA) qm = &sm.kr.qm[opaque(base)];
+  }
+  // wave-uniform packed metadata of row rr (mixed-width tiles)
+  __device__ __forceinline__ int meta(int rr) const {
+    if constexpr (SM::kKDA) return __builtin_amdgcn_readfirstlane(r[rr].meta);
+    else return 0;
   }
 };
 
@@ -292,7 +309,7 @@ __device__ __forceinline__ void xwave_sum(SM& sm, int slot, int lane, float* x) 
 // once that wave's row factors are done), KDA tiles in cross-wave slot 2.
 template <int D, typename SM>
 __device__ __forceinline__ float* max_slot(SM& sm, int w) {
-  if constexpr (SM::kKDA) return &sm.red[2][w][0];
+  if constexpr (SM::kKDA) return &sm.absT[0][0][0] + SM::kKdaMax + w * D;
   else return &sm.absT[w][0][0];
 }
 template <int D, typename SM>
@@ -368,7 +385,7 @@ __device__ __forceinline__ void scale_rows(float (&S)[32][G], const RW& rows, fl
     constexpr int r = CI(rr);
     const float ir = rows.r[r].ir;
     float iq = 0.0f;
-    if constexpr (KDA) iq = rows.r[r].iq;
+    if constexpr (KDA) iq = iqmax_of_meta(rows.meta(r));
     sfor<G>([&](auto gg) {
       constexpr int g = CI(gg);
       S[r][g] = S[r][g] * ir;
@@ -501,7 +518,12 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
     auto& rec = sm.row[row];
     // row factor: r_hat of a quantized row; 1 on pivot rows and FP16 pivot heads
     float rf = 1.0f;
-    if (rblk && !(KDA && A.P.pividx[(tile % A.P.H) * D + row] >= 0)) rf = h2f(rblk[row]);
+    int meta = 0;
+    if constexpr (KDA) {
+      meta = A.P.rowmeta[(tile % A.P.H) * D + row];
+      rec.meta = meta;
+    }
+    if (rblk && !(KDA && meta_pivot(meta))) rf = h2f(rblk[row]);
     float a = alpha;
     if constexpr (kRead) {
       const float beta = A.beta[tile];
@@ -510,7 +532,8 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
       const float ar = a * rf;
       rec.kr = A.P.order ? kk * ar : kk * rf;
       rec.bk = beta * kk;
-      rec.q = A.q[tile * D + row];
+      if constexpr (KDA) (&sm.absT[0][0][0])[SM::kKdaQ + row] = A.q[tile * D + row];
+      else rec.q = A.q[tile * D + row];
     }
     if constexpr (MODE == WRITE) {
       const float* st = A.stash + tile * 4 * D;
@@ -747,9 +770,6 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
   // a head whose rows are all FP16 pivots stores no row or column factors
   uint16_t* rblk = nwords > 0 ? reinterpret_cast<uint16_t*>(seg + A.P.off_r[h]) : nullptr;
   uint16_t* cblk = nwords > 0 ? reinterpret_cast<uint16_t*>(seg + A.P.off_c[h]) : nullptr;
-  const int* bitsv = A.P.bits + h * D;
-  const int* posv = A.P.rowpos + h * D;
-  const int* pidv = A.P.pividx + h * D;
   const Rows<SM> rows(sm);
   unsigned fl = 0;
   float S[R][G];
@@ -771,10 +791,6 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
   if constexpr (kWrite) {
     den = A.P.den[h * D + row];
     om = A.P.omega[h * D + row];
-    if (lane < 32) {
-      sm.row[row].iq = A.P.iq[h * D + row];
-      sm.kr.qm[row] = A.P.qmax[h * D + row];
-    }
   }
   __syncthreads();
 
@@ -782,15 +798,17 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
   if constexpr (MODE == ENCODE) {
     load_state<D>(A, tile, row0, lane, S);
   } else {
-    sfor<R>([&](auto rr) {
-      constexpr int r = CI(rr);
-      const int rw = row0 + r;
-      const int pv = __builtin_amdgcn_readfirstlane(pidv[rw]);
-      if (pv >= 0) {
-        sfor<G>([&](auto gg) { S[r][CI(gg)] = h2f(pblk[pv * D + G * lane + CI(gg)]); });
-      } else {
-        const int bw = __builtin_amdgcn_readfirstlane(bitsv[rw]);
-        const int p = __builtin_amdgcn_readfirstlane(posv[rw]);
+    // rows in groups of eight: the group's metadata first (one batch of broadcast reads), then
+    // its decode; a group without a pivot row (the common case) takes a branch-free path
+    sfor<R / 8>([&](auto qq) {
+      constexpr int r0 = 8 * CI(qq);
+      int ms[8];
+      sfor<8>([&](auto tt) { ms[CI(tt)] = rows.meta(r0 + CI(tt)); });
+      unsigned pmask = 0;
+      sfor<8>([&](auto tt) { pmask |= meta_pivot(ms[CI(tt)]) ? 1u << CI(tt) : 0u; });
+      auto decode = [&](auto tt) {
+        constexpr int t = CI(tt), r = r0 + t;
+        const int bw = meta_bits(ms[t]), p = meta_low(ms[t]);
         const uint32_t lo = sm.kc.code[(p >> 5) * 64 + lane];
         const uint32_t hi = sm.kc.code[((p >> 5) + 1) * 64 + lane];
         const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, p & 31);
@@ -798,6 +816,19 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
           constexpr int g = CI(gg);
           const int z = __builtin_amdgcn_sbfe((int)x, g * bw, bw);
           S[r][g] = cc[g] * (float)z;
+        });
+      };
+      if (pmask == 0) {
+        sfor<8>(decode);
+      } else {
+        sfor<8>([&](auto tt) {
+          constexpr int t = CI(tt), r = r0 + t;
+          if (meta_pivot(ms[t])) {
+            const int pv = meta_low(ms[t]);
+            sfor<G>([&](auto gg) { S[r][CI(gg)] = h2f(pblk[pv * D + G * lane + CI(gg)]); });
+          } else {
+            decode(tt);
+          }
         });
       }
     });
@@ -825,7 +856,8 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     });
     if constexpr (kRead) {
       float o[G];
-      row_dot<G>(S, [&](int r) { return rows.r[r].q; }, o);
+      const float* const qk = lds_pin(sm, &sm.absT[0][0][0] + SM::kKdaQ + row0);
+      row_dot<G>(S, [&](int r) { return qk[r]; }, o);
       xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
       xwave_sum<D>(sm, 1, lane, o);
@@ -839,7 +871,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
   if constexpr (kWrite) {
     put_rowabs<D>(sm, S, lane);
     wave_lds_sync();
-    const bool piv = A.P.pividx[h * D + row] >= 0;
+    const bool piv = meta_pivot(sm.row[row].meta);
     row_factor<D>(sm, lane, row, den, om, piv, rblk, fl);
     __syncthreads();  // absT dead for every wave: the code staging area is zeroed for packing
     {
@@ -851,8 +883,9 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     // ---- phase 3: pivot rows stored as binary16; y and c0 = max_i |y_ij| / qmax_i
     sfor<R>([&](auto rr) {
       constexpr int r = CI(rr);
-      const int pv = __builtin_amdgcn_readfirstlane(pidv[row0 + r]);
-      if (pv >= 0) {
+      const int m = rows.meta(r);
+      if (meta_pivot(m)) {
+        const int pv = meta_low(m);
         sfor<G>([&](auto gg) {
           const uint16_t hv = f2h(S[r][CI(gg)]);
           if (is_inf16(hv)) fl |= kFlagPivotOvf;
@@ -893,11 +926,11 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
       };
       sfor<R>([&](auto rr) {
         constexpr int r = CI(rr);
-        const int rw = row0 + r;
-        const int bw = __builtin_amdgcn_readfirstlane(bitsv[rw]);
-        if (__builtin_amdgcn_readfirstlane(pidv[rw]) < 0) {
-          const int p = __builtin_amdgcn_readfirstlane(posv[rw]);
-          const float qm = rows.qm[r];
+        const int m = rows.meta(r);
+        if (!meta_pivot(m)) {
+          const int bw = meta_bits(m);
+          const int p = meta_low(m);
+          const float qm = qmax_of_meta(m);
           const uint32_t mask = (1u << bw) - 1u;
           uint32_t wv = 0;
           sfor<G>([&](auto gg) {
@@ -971,7 +1004,7 @@ __global__ __launch_bounds__(Geo<D>::NT, 4) void k_gdn(StepArgs A) {
 }
 
 template <int D, int MODE>
-__global__ __launch_bounds__(Geo<D>::NT) void k_kda(StepArgs A) {
+__global__ __launch_bounds__(Geo<D>::NT, 4) void k_kda(StepArgs A) {
   __shared__ Smem<D, true> sm;
   const int tile = blockIdx.x;
   const int b = tile / A.P.H, h = tile - b * A.P.H;

@@ -36,6 +36,7 @@ struct DevPlan {
   const int* bits;           // [H*d] width (0 on pivot rows)
   const int* rowpos;         // [H*d] stream bit offset of the row's first code (-1 on pivots)
   const int* pividx;         // [H*d] row index inside the pivot block (-1 otherwise)
+  const int* rowmeta;        // [H*d] packed: pivot 0x80000000 | pividx, else rowpos | bits << 16
   unsigned* status;          // accumulated STEPQ_FLAG_* bits
 };
 

@@ -157,6 +157,20 @@ def algorithmic_bytes(w: synth.Workload, plan: "stepq.Plan") -> int:
     return w.B * (per_req + io)
 
 
+def code_bytes(w: synth.Workload, plan: "stepq.Plan") -> int:
+    """Packed-state bytes of one layer read once (codes, binary16 factors and pivots): what the
+    split mode's side-stream writeback reads a second time."""
+    d = w.d
+    total = 0
+    for h in range(plan.H):
+        b = plan.bits[h]
+        p = plan.pivot[h].astype(bool)
+        total += d * int(b[~p].astype(np.int64).sum()) // 8 + 2 * d * int(p.sum())
+        if (~p).any():
+            total += 2 * (d + d)
+    return w.B * total
+
+
 # Algorithmic ALU operations per state entry of one decode step, counted from the evaluation
 # order of the method (each binary32 multiply, add, fused multiply-add, maximum, rounding, clamp,
 # conversion and code extraction/insertion counts one; reductions over 128 rows cost
