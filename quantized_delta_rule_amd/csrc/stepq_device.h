@@ -880,21 +880,39 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
       for (int x = tid; x < n4; x += NT) l4[x] = u32x4{0u, 0u, 0u, 0u};
     }
 
-    // ---- phase 3: pivot rows stored as binary16; y and c0 = max_i |y_ij| / qmax_i
-    sfor<R>([&](auto rr) {
-      constexpr int r = CI(rr);
-      const int m = rows.meta(r);
-      if (meta_pivot(m)) {
-        const int pv = meta_low(m);
-        sfor<G>([&](auto gg) {
-          const uint16_t hv = f2h(S[r][CI(gg)]);
-          if (is_inf16(hv)) fl |= kFlagPivotOvf;
-          pblk[pv * D + G * lane + CI(gg)] = hv;
+    // ---- phase 3: pivot rows stored as binary16; y and c0 = max_i |y_ij| / qmax_i (rows in
+    // groups of eight: metadata and 1/qmax first, then the rows)
+    float mx[G];
+    sfor<G>([&](auto gg) { mx[CI(gg)] = 0.0f; });
+    sfor<R / 8>([&](auto qq) {
+      constexpr int r0 = 8 * CI(qq);
+      int ms[8];
+      sfor<8>([&](auto tt) { ms[CI(tt)] = rows.meta(r0 + CI(tt)); });
+      unsigned pmask = 0;
+      sfor<8>([&](auto tt) { pmask |= meta_pivot(ms[CI(tt)]) ? 1u << CI(tt) : 0u; });
+      if (pmask) {
+        sfor<8>([&](auto tt) {
+          constexpr int r = r0 + CI(tt);
+          if (meta_pivot(ms[CI(tt)])) {
+            const int pv = meta_low(ms[CI(tt)]);
+            sfor<G>([&](auto gg) {
+              const uint16_t hv = f2h(S[r][CI(gg)]);
+              if (is_inf16(hv)) fl |= kFlagPivotOvf;
+              pblk[pv * D + G * lane + CI(gg)] = hv;
+            });
+          }
         });
       }
+      sfor<8>([&](auto tt) {
+        constexpr int r = r0 + CI(tt);
+        const float ir = rows.r[r].ir, iq = iqmax_of_meta(ms[CI(tt)]);
+        sfor<G>([&](auto gg) {
+          constexpr int g = CI(gg);
+          S[r][g] = S[r][g] * ir;
+          mx[g] = __builtin_fmaxf(mx[g], __builtin_fabsf(S[r][g]) * iq);
+        });
+      });
     });
-    float mx[G];
-    scale_rows<G, true>(S, rows, mx);
     xwave_max_put<D>(sm, w, lane, mx);
     __syncthreads();  // also orders the zeroing above before the packing below
     xwave_max<D>(sm, lane, mx);
@@ -914,47 +932,38 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     xwave_sum<D>(sm, 1, lane, sq);
     col_factor<G>(num, sq, c0, w, lane, cblk, ic, fl);
 
-    // ---- phase 5: requantize and pack into the LDS stream (uniform positions), then copy out
-    {
-      unsigned long long acc = 0;
-      int cw = -1;         // word index held in the low half of acc
-      bool first = true;   // the wave's first word may be shared with the previous wave
-      auto flush = [&](bool shared) {
-        const uint32_t lo = (uint32_t)acc;
-        if (shared) atomicOr(&sm.kc.code[cw * 64 + lane], lo);
-        else sm.kc.code[cw * 64 + lane] = lo;
-      };
-      sfor<R>([&](auto rr) {
-        constexpr int r = CI(rr);
-        const int m = rows.meta(r);
+    // ---- phase 5: requantize and pack into the zeroed LDS stream, then copy out.  A row's G
+    // codes (G * b bits) land at its uniform stream position: OR-ed into one word, or two when
+    // they straddle a word boundary; words shared with a neighbouring wave's rows combine the
+    // same way.  The clamp bounds +-qmax in the offset domain are the integers 0x4B400000 +-
+    // qmax read as binary32 (the grid spacing there is 1).
+    sfor<R / 8>([&](auto qq) {
+      constexpr int r0 = 8 * CI(qq);
+      int ms[8];
+      sfor<8>([&](auto tt) { ms[CI(tt)] = rows.meta(r0 + CI(tt)); });
+      sfor<8>([&](auto tt) {
+        constexpr int r = r0 + CI(tt);
+        const int m = ms[CI(tt)];
         if (!meta_pivot(m)) {
-          const int bw = meta_bits(m);
-          const int p = meta_low(m);
-          const float qm = qmax_of_meta(m);
+          const int bw = meta_bits(m), p = meta_low(m);
+          const int qmi = (1 << (bw - 1)) - 1;
+          const float lo_b = __builtin_bit_cast(float, 0x4B400000 - qmi);
+          const float hi_b = __builtin_bit_cast(float, 0x4B400000 + qmi);
           const uint32_t mask = (1u << bw) - 1u;
           uint32_t wv = 0;
           sfor<G>([&](auto gg) {
             constexpr int g = CI(gg);
-            const uint32_t f = __builtin_bit_cast(uint32_t, quant_off(S[r][g], ic[g], qm)) & mask;
-            wv |= f << (g * bw);
+            const float t = __builtin_amdgcn_fmed3f(__builtin_fmaf(S[r][g], ic[g], kMagic), lo_b,
+                                                    hi_b);
+            wv |= (__builtin_bit_cast(uint32_t, t) & mask) << (g * bw);
           });
-          if (cw < 0) cw = p >> 5;
-          while ((p >> 5) > cw) {  // uniform: advance to the word holding this row's first bit
-            flush(first);
-            first = false;
-            acc >>= 32;
-            cw++;
-          }
-          acc |= (unsigned long long)wv << (p & 31);
+          const int sh = p & 31;
+          uint32_t* const dst = &sm.kc.code[(p >> 5) * 64 + lane];
+          atomicOr(dst, wv << sh);
+          if (sh + G * bw > 32) atomicOr(dst + 64, wv >> (32 - sh));
         }
       });
-      if (cw >= 0) {
-        flush(true);  // the last word may be shared with the next wave
-        // bits of a row that straddles past this word belong to word cw + 1
-        const uint32_t hi = (uint32_t)(acc >> 32);
-        if (hi) atomicOr(&sm.kc.code[(cw + 1) * 64 + lane], hi);
-      }
-    }
+    });
     __syncthreads();
     {
       const int n4 = nwords * 16;
