@@ -30,9 +30,11 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
 # build does not use).
 PEAK_ALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "decode head-steps/s + achieved HBM GB/s vs peak, nominal-6-bit GDN state pool"
-COUNTERS = os.path.join(ROOT, "profiles", "gdn6_70x48_counters.json")
+# counter summary of a workload (HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE)
+COUNTERS = os.path.join(ROOT, "profiles", "{name}_counters.json")
 KERNEL_SOURCES = ["quantized_delta_rule_amd/csrc/stepq_device.h",
                   "quantized_delta_rule_amd/csrc/stepq_k128_gdn.hip",
+                  "quantized_delta_rule_amd/csrc/stepq_k128_kda.hip",
                   "quantized_delta_rule_amd/csrc/stepq_internal.h"]
 
 
@@ -254,8 +256,9 @@ def main():
     kname = ("k_gdn" if w.kind == "gdn" else "k_kda") + f"<{w.d}, " + \
         ("READ> + WRITE (side stream)" if w.split else "FUSED>")
     traffic = None
-    if os.path.exists(COUNTERS):
-        c = json.load(open(COUNTERS))
+    cpath = COUNTERS.format(name=w.name)
+    if os.path.exists(cpath):
+        c = json.load(open(cpath))
         if c.get("kernel_sha") == kernel_sha() and c.get("workload") == w.name:
             traffic = c["hbm_bytes_per_launch"]
     unit_desc = (f"MC-DP map {w.choices}" if w.alloc == "mcdp" else
