@@ -135,20 +135,32 @@ struct Row<true> {
   int meta;                    // packed width, stream position or pivot index (row_meta)
 };
 
+// Read-only data in the constant address space: loads at wave-uniform addresses become scalar
+// loads through the scalar cache.
+template <typename T>
+using KConst = const __attribute__((address_space(4))) T;
+
+// A wave-uniform element of a read-only table (plan tables, slot indices): one scalar load.
+template <typename T>
+__device__ __forceinline__ T kread(const T* p, long long i) {
+  return ((KConst<T>*)p)[i];
+}
+
+// The same uniform pointer, made opaque to the optimizer: loads through it are not merged with
+// loads of the same data elsewhere (which would keep them live, in scalar registers, across
+// phases).
+template <typename T>
+__device__ __forceinline__ KConst<T>* opaque_s(KConst<T>* p) {
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
 // Per-row layout metadata of mixed-width tiles, packed by the plan into one int: a pivot row is
 // 0x80000000 | (its index in the pivot block); a quantized row is its stream bit position |
 // (width << 16).  Read once per row and phase as a wave-uniform scalar.
 __device__ __forceinline__ bool meta_pivot(int m) { return m < 0; }
 __device__ __forceinline__ int meta_low(int m) { return m & 0xFFFF; }  // pivot index / position
 __device__ __forceinline__ int meta_bits(int m) { return (m >> 16) & 15; }
-// qmax = 2^(b-1) - 1 and 1/qmax (binary32, correctly rounded) of a row by its packed metadata,
-// 0 for a pivot row: tables in constant memory, read with the wave-uniform index through the
-// scalar cache (no per-row selects in vector registers).
-__constant__ float kQmaxTab[5] = {0.0f, 1.0f, 7.0f, 31.0f, 127.0f};
-__constant__ float kIqmaxTab[5] = {0.0f, 1.0f, 1.0f / 7.0f, 1.0f / 31.0f, 1.0f / 127.0f};
-__device__ __forceinline__ int meta_width_class(int m) { return m < 0 ? 0 : ((m >> 16) & 15) >> 1; }
-__device__ __forceinline__ float qmax_of_meta(int m) { return kQmaxTab[meta_width_class(m)]; }
-__device__ __forceinline__ float iqmax_of_meta(int m) { return kIqmaxTab[meta_width_class(m)]; }
 template <int D, bool KDA>
 struct CodeKda {  // code block staging of mixed-width tiles
   uint32_t code[(2 * D * 8 / 32 + 1) * 64];
@@ -202,11 +214,6 @@ struct Rows {
   __device__ __forceinline__ Rows(const SM& sm) {
     const int base = (threadIdx.x >> 6) * 32;
     r = &sm.row[opaque(base)];
-  }
-  // wave-uniform packed metadata of row rr (mixed-width tiles)
-  __device__ __forceinline__ int meta(int rr) const {
-    if constexpr (SM::kKDA) return __builtin_amdgcn_readfirstlane(r[rr].meta);
-    else return 0;
   }
 };
 
@@ -376,21 +383,18 @@ __device__ __forceinline__ void row_factor(SM& sm, int lane, int row, float den,
   sm.row[row].W = (om * rf) * rf;
 }
 
-// y = S * ir (in place) and the column maximum max_i |y| (GDN: one width, the 1/qmax factor
-// is applied after the maximum -- rounding is monotone) or max_i |y| / qmax_i (KDA).
-template <int G, bool KDA, typename RW>
+// y = S * ir (in place) and the column maximum max_i |y| of a one-width (GDN) tile: the 1/qmax
+// factor is applied after the maximum (rounding is monotone).
+template <int G, typename RW>
 __device__ __forceinline__ void scale_rows(float (&S)[32][G], const RW& rows, float* mx) {
   sfor<G>([&](auto gg) { mx[CI(gg)] = 0.0f; });
   sfor<32>([&](auto rr) {
     constexpr int r = CI(rr);
     const float ir = rows.r[r].ir;
-    float iq = 0.0f;
-    if constexpr (KDA) iq = iqmax_of_meta(rows.meta(r));
     sfor<G>([&](auto gg) {
       constexpr int g = CI(gg);
       S[r][g] = S[r][g] * ir;
-      if constexpr (KDA) mx[g] = __builtin_fmaxf(mx[g], __builtin_fabsf(S[r][g]) * iq);
-      else mx[g] = __builtin_fmaxf(mx[g], __builtin_fabsf(S[r][g]));
+      mx[g] = __builtin_fmaxf(mx[g], __builtin_fabsf(S[r][g]));
     });
   });
 }
@@ -560,11 +564,11 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
   constexpr bool kWrite = MODE != READ;                   // refits and packs
   const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
   const long long tile = (long long)b * A.P.H + h;
-  uint8_t* seg = A.pool + slot * A.P.bpr + A.P.head_off[h];
+  uint8_t* seg = A.pool + slot * A.P.bpr + kread(A.P.head_off, h);
   // this lane's code words: word x of the wave's rows at wl[64 x] (one base, immediate offsets)
   uint32_t* const wl = reinterpret_cast<uint32_t*>(seg) + (w * WPW * 64 + lane);
-  uint16_t* rblk = reinterpret_cast<uint16_t*>(seg + A.P.off_r[h]);
-  uint16_t* cblk = reinterpret_cast<uint16_t*>(seg + A.P.off_c[h]);
+  uint16_t* rblk = reinterpret_cast<uint16_t*>(seg + kread(A.P.off_r, h));
+  uint16_t* cblk = reinterpret_cast<uint16_t*>(seg + kread(A.P.off_c, h));
   const Rows<SM> rows(sm);
   unsigned fl = 0;
 
@@ -638,7 +642,7 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
 
     // ---- phase 3: y = S / r_hat, first column factor c0 = max_i |y_ij| / qmax
     float mx[G];
-    scale_rows<G, false>(S, rows, mx);
+    scale_rows<G>(S, rows, mx);
     xwave_max_put<D>(sm, w, lane, mx);
     __syncthreads();
     xwave_max<D>(sm, lane, mx);
@@ -683,7 +687,7 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, long long s
   constexpr bool kWrite = MODE != READ;
   const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
   const long long tile = (long long)b * A.P.H + h;
-  uint8_t* seg = A.pool + slot * A.P.bpr + A.P.head_off[h];
+  uint8_t* seg = A.pool + slot * A.P.bpr + kread(A.P.head_off, h);
   uint16_t* hblk = reinterpret_cast<uint16_t*>(seg);
   const Rows<SM> rows(sm);
   unsigned fl = 0;
@@ -763,14 +767,17 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
   const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
   const int tid = threadIdx.x;
   const long long tile = (long long)b * A.P.H + h;
-  uint8_t* seg = A.pool + slot * A.P.bpr + A.P.head_off[h];
+  uint8_t* seg = A.pool + slot * A.P.bpr + kread(A.P.head_off, h);
   uint32_t* words = reinterpret_cast<uint32_t*>(seg);
-  uint16_t* pblk = reinterpret_cast<uint16_t*>(seg + A.P.off_piv[h]);
-  const int nwords = A.P.words[h];
+  uint16_t* pblk = reinterpret_cast<uint16_t*>(seg + kread(A.P.off_piv, h));
+  const int nwords = kread(A.P.words, h);
   // a head whose rows are all FP16 pivots stores no row or column factors
-  uint16_t* rblk = nwords > 0 ? reinterpret_cast<uint16_t*>(seg + A.P.off_r[h]) : nullptr;
-  uint16_t* cblk = nwords > 0 ? reinterpret_cast<uint16_t*>(seg + A.P.off_c[h]) : nullptr;
+  uint16_t* rblk = nwords > 0 ? reinterpret_cast<uint16_t*>(seg + kread(A.P.off_r, h)) : nullptr;
+  uint16_t* cblk = nwords > 0 ? reinterpret_cast<uint16_t*>(seg + kread(A.P.off_c, h)) : nullptr;
   const Rows<SM> rows(sm);
+  // the wave's row metadata and 1/qmax, read in groups of eight through the scalar cache
+  KConst<int>* const gmeta = (KConst<int>*)(A.P.rowmeta + (h * D + row0));
+  KConst<float>* const giq = (KConst<float>*)(A.P.iq + (h * D + row0));
   unsigned fl = 0;
   float S[R][G];
   float e[G], u[G], vv[G], cc[G];
@@ -798,14 +805,15 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
   if constexpr (MODE == ENCODE) {
     load_state<D>(A, tile, row0, lane, S);
   } else {
-    // rows in groups of eight: the group's metadata first (one batch of broadcast reads), then
+    // rows in groups of eight: the group's metadata first (one scalar load of eight words), then
     // its decode; a group without a pivot row (the common case) takes a branch-free path
     sfor<R / 8>([&](auto qq) {
       constexpr int r0 = 8 * CI(qq);
       int ms[8];
-      sfor<8>([&](auto tt) { ms[CI(tt)] = rows.meta(r0 + CI(tt)); });
-      unsigned pmask = 0;
-      sfor<8>([&](auto tt) { pmask |= meta_pivot(ms[CI(tt)]) ? 1u << CI(tt) : 0u; });
+      KConst<int>* const gm = opaque_s(gmeta);
+      sfor<8>([&](auto tt) { ms[CI(tt)] = gm[r0 + CI(tt)]; });
+      int any = 0;  // sign bit set: the group holds a pivot row
+      sfor<8>([&](auto tt) { any |= ms[CI(tt)]; });
       auto decode = [&](auto tt) {
         constexpr int t = CI(tt), r = r0 + t;
         const int bw = meta_bits(ms[t]), p = meta_low(ms[t]);
@@ -818,7 +826,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
           S[r][g] = cc[g] * (float)z;
         });
       };
-      if (pmask == 0) {
+      if (!meta_pivot(any)) {
         sfor<8>(decode);
       } else {
         sfor<8>([&](auto tt) {
@@ -887,10 +895,14 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     sfor<R / 8>([&](auto qq) {
       constexpr int r0 = 8 * CI(qq);
       int ms[8];
-      sfor<8>([&](auto tt) { ms[CI(tt)] = rows.meta(r0 + CI(tt)); });
-      unsigned pmask = 0;
-      sfor<8>([&](auto tt) { pmask |= meta_pivot(ms[CI(tt)]) ? 1u << CI(tt) : 0u; });
-      if (pmask) {
+      float iqs[8];
+      KConst<int>* const gm = opaque_s(gmeta);
+      KConst<float>* const gq = opaque_s(giq);
+      sfor<8>([&](auto tt) { ms[CI(tt)] = gm[r0 + CI(tt)]; });
+      sfor<8>([&](auto tt) { iqs[CI(tt)] = gq[r0 + CI(tt)]; });
+      int any = 0;  // sign bit set: the group holds a pivot row
+      sfor<8>([&](auto tt) { any |= ms[CI(tt)]; });
+      if (meta_pivot(any)) {
         sfor<8>([&](auto tt) {
           constexpr int r = r0 + CI(tt);
           if (meta_pivot(ms[CI(tt)])) {
@@ -905,7 +917,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
       }
       sfor<8>([&](auto tt) {
         constexpr int r = r0 + CI(tt);
-        const float ir = rows.r[r].ir, iq = iqmax_of_meta(ms[CI(tt)]);
+        const float ir = rows.r[r].ir, iq = iqs[CI(tt)];
         sfor<G>([&](auto gg) {
           constexpr int g = CI(gg);
           S[r][g] = S[r][g] * ir;
@@ -940,7 +952,8 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     sfor<R / 8>([&](auto qq) {
       constexpr int r0 = 8 * CI(qq);
       int ms[8];
-      sfor<8>([&](auto tt) { ms[CI(tt)] = rows.meta(r0 + CI(tt)); });
+      KConst<int>* const gm = opaque_s(gmeta);
+      sfor<8>([&](auto tt) { ms[CI(tt)] = gm[r0 + CI(tt)]; });
       sfor<8>([&](auto tt) {
         constexpr int r = r0 + CI(tt);
         const int m = ms[CI(tt)];
@@ -985,7 +998,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
 template <int MODE>
 __device__ __forceinline__ long long pool_slot(const StepArgs& A, int b, int h) {
   if (!A.slots) return b;
-  const int s = A.slots[b];
+  const int s = kread(A.slots, b);
   const bool valid = s >= 0 && s < A.n_slots;
   if (h == 0 && threadIdx.x == 0) {
     if (MODE == READ) A.slot_out[b] = valid ? s : -1;
@@ -1000,10 +1013,10 @@ template <int D, int MODE>
 __global__ __launch_bounds__(Geo<D>::NT, 4) void k_gdn(StepArgs A) {
   __shared__ Smem<D, false> sm;
   const int hs = blockIdx.x / A.B, b = blockIdx.x - hs * A.B;
-  const int h = A.P.head_order[hs];
+  const int h = kread(A.P.head_order, hs);
   const long long slot = pool_slot<MODE>(A, b, h);
   if (slot < 0) return;
-  switch (A.P.head_type[h]) {
+  switch (kread(A.P.head_type, h)) {
     case 2: gdn_tile<D, MODE, 2>(A, b, slot, h, sm); break;
     case 4: gdn_tile<D, MODE, 4>(A, b, slot, h, sm); break;
     case 6: gdn_tile<D, MODE, 6>(A, b, slot, h, sm); break;
