@@ -497,7 +497,7 @@ __device__ __forceinline__ void load_state(const StepArgs& A, long long tile, in
 // carries u and v (per-row e) instead of e.  The key-projection coefficient of a row is k_i r_i,
 // or k_i (a_i r_i) when the gate decays the rows before the delta update (plan order 1).
 template <int D, int MODE, bool KDA, bool UV = KDA, typename SM>
-__device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long tile,
+__device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long tile, int h,
                                             int lane, int row, const uint16_t* rblk,
                                             float& alpha, float* vv, float* e, float* u) {
   constexpr int G = Geo<D>::G;
@@ -518,32 +518,39 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
       sfor<G>([&](auto gg) { e[CI(gg)] = st[2 * D + G * lane + CI(gg)]; });
     }
   }
+  // Every load first, in all lanes (lanes 32..63 read the same rows as lanes 0..31), then the
+  // arithmetic and the record writes of lanes 0..31: the tile waits for memory once.  Without
+  // stored row factors (FP16 pivot heads, encoding) a 16-bit word of the head's den row is read
+  // in their place and not used.
+  const uint16_t* const rsrc = rblk ? rblk : reinterpret_cast<const uint16_t*>(A.P.den + h * D);
+  const uint16_t rh = rsrc[row];
+  int meta = 0;
+  if constexpr (KDA) meta = A.P.rowmeta[h * D + row];
+  float a = alpha, beta = 0.0f, kk = 0.0f, qv = 0.0f, bk = 0.0f;
+  if constexpr (kRead) {
+    beta = A.beta[tile];
+    kk = A.k[tile * D + row];
+    qv = A.q[tile * D + row];
+    if constexpr (KDA) a = A.alpha[tile * D + row];
+  }
+  if constexpr (MODE == WRITE) {
+    const float* st = A.stash + tile * 4 * D;
+    a = st[row];
+    bk = st[D + row];
+  }
   if (lane < 32) {
     auto& rec = sm.row[row];
     // row factor: r_hat of a quantized row; 1 on pivot rows and FP16 pivot heads
-    float rf = 1.0f;
-    int meta = 0;
-    if constexpr (KDA) {
-      meta = A.P.rowmeta[(tile % A.P.H) * D + row];
-      rec.meta = meta;
-    }
-    if (rblk && !(KDA && meta_pivot(meta))) rf = h2f(rblk[row]);
-    float a = alpha;
+    const float rf = rblk && !(KDA && meta_pivot(meta)) ? h2f(rh) : 1.0f;
+    if constexpr (KDA) rec.meta = meta;
     if constexpr (kRead) {
-      const float beta = A.beta[tile];
-      const float kk = A.k[tile * D + row];
-      if constexpr (KDA) a = A.alpha[tile * D + row];
       const float ar = a * rf;
       rec.kr = A.P.order ? kk * ar : kk * rf;
       rec.bk = beta * kk;
-      if constexpr (KDA) (&sm.absT[0][0][0])[SM::kKdaQ + row] = A.q[tile * D + row];
-      else rec.q = A.q[tile * D + row];
+      if constexpr (KDA) (&sm.absT[0][0][0])[SM::kKdaQ + row] = qv;
+      else rec.q = qv;
     }
-    if constexpr (MODE == WRITE) {
-      const float* st = A.stash + tile * 4 * D;
-      a = st[row];
-      rec.bk = st[D + row];
-    }
+    if constexpr (MODE == WRITE) rec.bk = bk;
     if constexpr (KDA) rec.a = a;
     rec.ar = a * rf;
   }
@@ -584,13 +591,13 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
     });
     sfor<G>([&](auto gg) { cc[CI(gg)] = h2f(cblk[G * lane + CI(gg)]); });
   }
-  load_inputs<D, MODE, false>(A, sm, tile, lane, row, MODE != ENCODE ? rblk : nullptr, alpha,
-                              vv, e, u);
   float den = 1.0f, om = 0.0f;
   if constexpr (kWrite) {
     den = A.P.den[h * D + row];
     om = A.P.omega[h * D + row];
   }
+  load_inputs<D, MODE, false>(A, sm, tile, h, lane, row, MODE != ENCODE ? rblk : nullptr, alpha,
+                              vv, e, u);
   wave_lds_sync();
 
   if constexpr (MODE == ENCODE) {
@@ -704,7 +711,7 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, long long s
       });
     });
   }
-  load_inputs<D, MODE, false>(A, sm, tile, lane, row, nullptr, alpha, vv, e, u);
+  load_inputs<D, MODE, false>(A, sm, tile, h, lane, row, nullptr, alpha, vv, e, u);
   wave_lds_sync();
   if constexpr (MODE != ENCODE) {
     if constexpr (kRead) {
@@ -764,6 +771,8 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
   constexpr bool kRead = MODE == FUSED || MODE == READ;
   constexpr bool kWrite = MODE != READ;
   constexpr bool kUV = ORDER == 0;  // split-mode hand-over carries u and v (per-row error)
+  // passes of the workgroup over the largest code block (8-bit rows), in 16-byte units
+  constexpr int kStageIt = (G * D * 8 / 32 * 16 + NT - 1) / NT;
   const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
   const int tid = threadIdx.x;
   const long long tile = (long long)b * A.P.H + h;
@@ -783,21 +792,35 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
   float e[G], u[G], vv[G], cc[G];
   float alpha = 0.0f;
 
-  // ---- phase 0: stage the code block in LDS (coalesced 16-byte copies), per-row inputs
+  // ---- phase 0: stage the code block in LDS (coalesced 16-byte copies), per-row inputs.  Every
+  // global load of the phase is issued before the first LDS write, so the tile waits for memory
+  // once.  The column factors are read unconditionally: a head without them (all rows pivots)
+  // reads its pivot block instead and never uses the values.
+  const int n4 = nwords * 16;  // 16-byte units: nwords * 64 lanes * 4 bytes / 16
+  u32x4* const l4 = reinterpret_cast<u32x4*>(sm.kc.code);
+  u32x4 st[kStageIt];
   if constexpr (MODE != ENCODE) {
-    const int n4 = nwords * 16;  // 16-byte units: nwords * 64 lanes * 4 bytes / 16
     const u32x4* g4 = reinterpret_cast<const u32x4*>(words);
-    u32x4* l4 = reinterpret_cast<u32x4*>(sm.kc.code);
-    for (int x = tid; x < n4; x += NT) l4[x] = __builtin_nontemporal_load(&g4[x]);
-    if (tid < 16) l4[n4 + tid] = u32x4{0u, 0u, 0u, 0u};  // window over the last word
-    sfor<G>([&](auto gg) { cc[CI(gg)] = cblk ? h2f(cblk[G * lane + CI(gg)]) : 0.0f; });
+    sfor<kStageIt>([&](auto ii) {
+      const int x = tid + CI(ii) * NT;
+      if (x < n4) st[CI(ii)] = __builtin_nontemporal_load(&g4[x]);
+    });
+    const uint16_t* const cread = nwords > 0 ? cblk : pblk;
+    sfor<G>([&](auto gg) { cc[CI(gg)] = h2f(cread[G * lane + CI(gg)]); });
   }
-  load_inputs<D, MODE, true, kUV>(A, sm, tile, lane, row, MODE != ENCODE ? rblk : nullptr, alpha, vv,
-                             e, u);
   float den = 1.0f, om = 0.0f;
   if constexpr (kWrite) {
     den = A.P.den[h * D + row];
     om = A.P.omega[h * D + row];
+  }
+  load_inputs<D, MODE, true, kUV>(A, sm, tile, h, lane, row, MODE != ENCODE ? rblk : nullptr,
+                                  alpha, vv, e, u);
+  if constexpr (MODE != ENCODE) {
+    sfor<kStageIt>([&](auto ii) {
+      const int x = tid + CI(ii) * NT;
+      if (x < n4) l4[x] = st[CI(ii)];
+    });
+    if (tid < 16) l4[n4 + tid] = u32x4{0u, 0u, 0u, 0u};  // window over the last word
   }
   __syncthreads();
 
@@ -982,7 +1005,15 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
       const int n4 = nwords * 16;
       u32x4* g4 = reinterpret_cast<u32x4*>(words);
       const u32x4* l4 = reinterpret_cast<const u32x4*>(sm.kc.code);
-      for (int x = tid; x < n4; x += NT) __builtin_nontemporal_store(l4[x], &g4[x]);
+      u32x4 st[kStageIt];
+      sfor<kStageIt>([&](auto ii) {
+        const int x = tid + CI(ii) * NT;
+        if (x < n4) st[CI(ii)] = l4[x];
+      });
+      sfor<kStageIt>([&](auto ii) {
+        const int x = tid + CI(ii) * NT;
+        if (x < n4) __builtin_nontemporal_store(st[CI(ii)], &g4[x]);
+      });
     }
   }
   raise_flags(A, fl);
