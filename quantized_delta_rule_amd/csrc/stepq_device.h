@@ -1047,12 +1047,19 @@ __global__ __launch_bounds__(Geo<D>::NT, 4) void k_gdn(StepArgs A) {
   const int h = kread(A.P.head_order, hs);
   const long long slot = pool_slot<MODE>(A, b, h);
   if (slot < 0) return;
+  // Each tile path reads the arguments it uses itself, through an opaque pointer to the kernel
+  // argument segment: argument values shared by several paths are then not loaded once before
+  // the switch and held live across it (which spilled about 20 scalar registers per tile).
+  auto args = [&]() -> const StepArgs& {
+    KConst<StepArgs>* const p = (KConst<StepArgs>*)__builtin_amdgcn_kernarg_segment_ptr();
+    return *(const StepArgs*)opaque_s(p);
+  };
   switch (kread(A.P.head_type, h)) {
-    case 2: gdn_tile<D, MODE, 2>(A, b, slot, h, sm); break;
-    case 4: gdn_tile<D, MODE, 4>(A, b, slot, h, sm); break;
-    case 6: gdn_tile<D, MODE, 6>(A, b, slot, h, sm); break;
-    case 8: gdn_tile<D, MODE, 8>(A, b, slot, h, sm); break;
-    default: pivot_tile<D, MODE>(A, b, slot, h, sm); break;
+    case 2: gdn_tile<D, MODE, 2>(args(), b, slot, h, sm); break;
+    case 4: gdn_tile<D, MODE, 4>(args(), b, slot, h, sm); break;
+    case 6: gdn_tile<D, MODE, 6>(args(), b, slot, h, sm); break;
+    case 8: gdn_tile<D, MODE, 8>(args(), b, slot, h, sm); break;
+    default: pivot_tile<D, MODE>(args(), b, slot, h, sm); break;
   }
 }
 
