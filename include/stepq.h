@@ -125,6 +125,10 @@ int stepq_encode_state(stepq_plan_t plan, const float* S, void* pool, int B, voi
  * complete when the side stream's work is, and the next call on this plan (any pool) makes
  * `stream` wait for it.  In split mode the inputs are consumed by the stream-side kernel; the
  * caller may reuse them once the work on `stream` has completed.
+ * Graph capture: a fused plan's decode, encode and unpack calls only enqueue kernels on
+ * `stream`, so they may be captured into a HIP graph and replayed (each replay is one more step
+ * on the same buffers).  A split-mode plan returns STEPQ_ERR_UNSUPPORTED on a capturing stream:
+ * its side stream is joined back lazily, by the plan's next call.
  */
 int stepq_decode_step(stepq_plan_t plan, void* pool, int B, const float* q, const float* k,
                       const float* v, const float* alpha, const float* beta, float* out,

@@ -103,6 +103,18 @@ hipError_t wait_writeback(stepq_plan* p, hipStream_t stream) {
   return hipSuccess;
 }
 
+// A split-mode plan joins its side stream back lazily (the next call waits for the pending
+// writeback), which a stream capture cannot express: such plans refuse to run on a capturing
+// stream.  Fused plans enqueue kernels only and can be captured.
+int refuse_capture(stepq_plan* p, hipStream_t stream, const char* what) {
+  if (p->mode != STEPQ_MODE_SPLIT) return STEPQ_OK;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) == hipSuccess && st != hipStreamCaptureStatusNone)
+    return fail(STEPQ_ERR_UNSUPPORTED, "%s: a split-mode plan cannot run on a capturing stream "
+                "(use a fused plan inside graphs)", what);
+  return STEPQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -356,6 +368,7 @@ int encode_impl(stepq_plan_t p, const float* S, void* pool, int n_slots, const i
     return fail(STEPQ_ERR_INVALID_ARG, "B = %d exceeds max_batch %d", B, p->max_batch);
   DeviceGuard dg(p->device);
   hipStream_t s = (hipStream_t)stream;
+  if (int rc = refuse_capture(p, s, "encode")) return rc;
   HIP_TRY(wait_writeback(p, s));
   StepArgs a{};
   a.P = p->dp;
@@ -379,6 +392,7 @@ int decode_impl(stepq_plan_t p, void* pool, int n_slots, const int32_t* slots, i
   if (B == 0) return ok();
   DeviceGuard dg(p->device);
   hipStream_t s = (hipStream_t)stream;
+  if (int rc = refuse_capture(p, s, "decode_step")) return rc;
   StepArgs a{};
   a.P = p->dp;
   a.pool = (uint8_t*)pool;
@@ -449,6 +463,7 @@ int stepq_unpack_debug(stepq_plan_t p, const void* pool, int B, float* S_hat, ui
   if (int rc = check_pool(pool, B)) return rc;
   DeviceGuard dg(p->device);
   hipStream_t s = (hipStream_t)stream;
+  if (int rc = refuse_capture(p, s, "unpack_debug")) return rc;
   HIP_TRY(wait_writeback(p, s));
   HIP_TRY(launch_unpack(p->dp, (const uint8_t*)pool, B, S_hat, r, c, z, s));
   return ok();
