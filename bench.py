@@ -221,7 +221,7 @@ def main():
     # a side stream carries part of the work (split)
     step_ms = ms_per_step if w.split else avg_k * launches
 
-    k_ms, hot_ms = None, None
+    k_ms, hot_ms, graph_ms = None, None, None
     if not multi:
         # spread over launches (outside the timed region): each launch between its own event
         # pair, so these figures include that pair's overhead
@@ -242,6 +242,28 @@ def main():
         h1.record()
         drain()
         hot_ms = h0.elapsed_time(h1) / 50
+        if not w.split:
+            # graph replay (labelled, not the headline): one captured step per replica, the
+            # graph replayed back to back, so no step pays a host-side launch
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                for r in range(R):
+                    if step_fn(*(steps[r][0][:-1] + (cs,))):
+                        raise RuntimeError(L.stepq_last_error().decode())
+            g.replay()
+            drain()
+            reps = max(1, args.steps // R)
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record()
+            for _ in range(reps):
+                g.replay()
+            g1.record()
+            drain()
+            graph_ms = g0.elapsed_time(g1) / (reps * R)
+            del g
+        if any(p.status() != 0 for p in plans):
+            raise RuntimeError("status flags raised during the benchmark")
 
     if args.copy_calib:
         src = torch.empty(2 ** 28, dtype=torch.float32, device=dev)
@@ -284,6 +306,9 @@ def main():
                                                            for p in (10, 50, 90)]
         config["cache_hot_single_pool_kernel_ms"] = hot_ms
         config["cache_hot_single_pool_GBps"] = alg_bytes / (hot_ms * 1e-3) / 1e9
+    if graph_ms is not None:
+        config["graph_replay_ms_per_step"] = graph_ms
+        config["graph_replay_head_steps_per_s"] = heads / (graph_ms * 1e-3)
     if w.split:
         config["split_code_reread_bytes_per_step"] = sum(
             planning.code_bytes(w, p) for p in plans)
