@@ -39,7 +39,8 @@ typedef struct stepq_plan* stepq_plan_t;
 
 enum {
   STEPQ_OK = 0,
-  STEPQ_ERR_INVALID_ARG = -1, /* bad pointer, size, width, omega, batch ...             */
+  STEPQ_ERR_INVALID_ARG = -1, /* bad pointer, size, width, omega, batch (B < 0, B above
+                                 max_batch in split mode, B * n_heads above INT_MAX) ...   */
   STEPQ_ERR_UNSUPPORTED = -2, /* valid but not built (e.g. d_k != d_v)                   */
   STEPQ_ERR_HIP = -3,         /* a HIP runtime call failed; message has the HIP error    */
   STEPQ_ERR_OOM = -4,         /* device or host allocation failed                        */

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -101,6 +102,14 @@ void destroy_plan(stepq_plan* p) {
 hipError_t wait_writeback(stepq_plan* p, hipStream_t stream) {
   if (p->mode == STEPQ_MODE_SPLIT && p->write_pending) return hipStreamWaitEvent(stream, p->ev_write, 0);
   return hipSuccess;
+}
+
+// One workgroup per (request, head): B * n_heads must fit the launch grid's x dimension.
+int check_grid(const stepq_plan* p, int B) {
+  if ((long long)B * p->H > INT_MAX)
+    return fail(STEPQ_ERR_INVALID_ARG, "B * n_heads = %lld exceeds the launch grid",
+                (long long)B * p->H);
+  return STEPQ_OK;
 }
 
 // A split-mode plan joins its side stream back lazily (the next call waits for the pending
@@ -364,6 +373,7 @@ namespace {
 int encode_impl(stepq_plan_t p, const float* S, void* pool, int n_slots, const int32_t* slots,
                 int B, void* stream) {
   if (B > 0 && !S) return fail(STEPQ_ERR_INVALID_ARG, "S is NULL");
+  if (int rc = check_grid(p, B)) return rc;
   if (p->mode == STEPQ_MODE_SPLIT && B > p->max_batch)
     return fail(STEPQ_ERR_INVALID_ARG, "B = %d exceeds max_batch %d", B, p->max_batch);
   DeviceGuard dg(p->device);
@@ -387,6 +397,7 @@ int decode_impl(stepq_plan_t p, void* pool, int n_slots, const int32_t* slots, i
                 const float* beta, float* out, void* stream) {
   if (B > 0 && (!q || !k || !v || !alpha || !beta || !out))
     return fail(STEPQ_ERR_INVALID_ARG, "q, k, v, alpha, beta and out must be non-NULL");
+  if (int rc = check_grid(p, B)) return rc;
   if (p->mode == STEPQ_MODE_SPLIT && B > p->max_batch)
     return fail(STEPQ_ERR_INVALID_ARG, "B = %d exceeds max_batch %d", B, p->max_batch);
   if (B == 0) return ok();
@@ -463,6 +474,7 @@ int stepq_unpack_debug(stepq_plan_t p, const void* pool, int B, float* S_hat, ui
   if (int rc = check_pool(pool, B)) return rc;
   DeviceGuard dg(p->device);
   hipStream_t s = (hipStream_t)stream;
+  if (int rc = check_grid(p, B)) return rc;
   if (int rc = refuse_capture(p, s, "unpack_debug")) return rc;
   HIP_TRY(wait_writeback(p, s));
   HIP_TRY(launch_unpack(p->dp, (const uint8_t*)pool, B, S_hat, r, c, z, s));
