@@ -165,7 +165,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   // per-head layout (segment: code block, pivot rows, row factors, column factors)
   std::vector<int> head_type(H), off_piv(H), off_r(H), off_c(H), words(H);
   std::vector<long long> head_off(H), head_bytes(H);
-  std::vector<float> den(nrow), qmax(nrow), iq(nrow), omega(d->omega, d->omega + nrow);
+  std::vector<float> den(nrow), iq(nrow), omega(d->omega, d->omega + nrow);
   std::vector<int> bits(nrow), rowpos(nrow), pividx(nrow), rowmeta(nrow);
   long long off = 0;
   for (int h = 0; h < H; h++) {
@@ -181,7 +181,6 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
         pividx[r] = npiv++;
         rowpos[r] = -1;
         bits[r] = 0;
-        qmax[r] = 0.0f;
         iq[r] = 0.0f;
       } else {
         pividx[r] = -1;
@@ -189,8 +188,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
         rowmeta[r] = (int)lane_bits | (hb[i] << 16);
         bits[r] = hb[i];
         lane_bits += (long long)G * hb[i];
-        qmax[r] = (float)((1 << (hb[i] - 1)) - 1);
-        iq[r] = 1.0f / qmax[r];
+        iq[r] = 1.0f / (float)((1 << (hb[i] - 1)) - 1);
         if (b0 < 0) b0 = hb[i];
         else if (hb[i] != b0) uniform = false;
       }
@@ -267,7 +265,6 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   const size_t i_w = add(words.data(), H * sizeof(int));
   const size_t i_den = add(den.data(), nrow * sizeof(float));
   const size_t i_om = add(omega.data(), nrow * sizeof(float));
-  const size_t i_qm = add(qmax.data(), nrow * sizeof(float));
   const size_t i_iq = add(iq.data(), nrow * sizeof(float));
   const size_t i_bits = add(bits.data(), nrow * sizeof(int));
   const size_t i_pos = add(rowpos.data(), nrow * sizeof(int));
@@ -302,7 +299,6 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   dp.words = (const int*)at(i_w);
   dp.den = (const float*)at(i_den);
   dp.omega = (const float*)at(i_om);
-  dp.qmax = (const float*)at(i_qm);
   dp.iq = (const float*)at(i_iq);
   dp.bits = (const int*)at(i_bits);
   dp.rowpos = (const int*)at(i_pos);

@@ -31,7 +31,6 @@ struct DevPlan {
   const int* words;          // [H] words per lane of the code block
   const float* den;          // [H*d] 1 + omega_i / mean(omega)
   const float* omega;        // [H*d]
-  const float* qmax;         // [H*d] 2^(b-1)-1, 0 on pivot rows
   const float* iq;           // [H*d] 1/qmax, 0 on pivot rows
   const int* bits;           // [H*d] width (0 on pivot rows)
   const int* rowpos;         // [H*d] stream bit offset of the row's first code (-1 on pivots)
