@@ -80,6 +80,18 @@ def test_kda_allows_mixed_rows_until_the_device_check(sq):
         sq.Plan(sq.KDA, bits, np.zeros_like(bits, np.uint8), np.ones(bits.shape, np.float32))
 
 
+def test_c_client_is_built_and_needs_a_device():
+    # the plain-C client links the library and the HIP runtime; without a GPU it exits with 2
+    import subprocess
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("has a GPU (the client runs in tests/test_gpu_c_abi.py)")
+    client = os.path.join(ROOT, "tests", "c", "abi_client")
+    assert os.path.exists(client), "run __graft_entry__.build() first"
+    res = subprocess.run([client], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 2 and "no GPU" in res.stderr, (res.returncode, res.stderr)
+
+
 def test_lifetime_weights_match_oracle(sq, orc):
     l = np.random.default_rng(0).uniform(-0.2, -0.001, 200)
     l[0] = 0.0
