@@ -147,10 +147,16 @@ def main():
     alg_bytes = sum(planning.algorithmic_bytes(w, p) for p in plans)
     alg_ops = sum(planning.algorithmic_ops(w, p) for p in plans)
     pools, inputs, S_sample = [], [], {}
+    enc_ms = []
     for i, (plan, seed) in enumerate(units):
         S0 = warm_state(w, seed, dev)
         pool = plan.alloc_pool(w.B)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         plan.encode(S0, pool, w.B)
+        e1.record()
+        e1.synchronize()
+        enc_ms.append(e0.elapsed_time(e1))
         if i == 0 and not args.no_cpu:
             pick = [b * w.H + h for b, h in zip(range(0, w.B, max(1, w.B // w.H)), range(w.H))]
             S_sample = {t: S0[t].cpu().numpy() for t in pick}
@@ -309,6 +315,13 @@ def main():
     if graph_ms is not None:
         config["graph_replay_ms_per_step"] = graph_ms
         config["graph_replay_head_steps_per_s"] = heads / (graph_ms * 1e-3)
+    # encoding an fp32 state into the pool (the hand-off from prefill): the median over the
+    # setup encodes, each between its own event pair; bytes = fp32 state read + packed write
+    enc = float(np.median(enc_ms[1:] if len(enc_ms) > 1 else enc_ms))
+    enc_bytes = w.B * w.H * w.d * w.d * 4 + w.B * float(np.mean([p.bytes_per_request for p in plans]))
+    config["encode"] = {"kernel": kname.split("<")[0] + f"<{w.d}, ENCODE>", "ms_per_batch": enc,
+                        "bytes_per_batch": enc_bytes, "GBps": enc_bytes / (enc * 1e-3) / 1e9,
+                        "hbm_frac": enc_bytes / (enc * 1e-3) / 1e9 / PEAK_HBM_GBS}
     if w.split:
         config["split_code_reread_bytes_per_step"] = sum(
             planning.code_bytes(w, p) for p in plans)
