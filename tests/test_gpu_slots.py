@@ -169,3 +169,37 @@ def test_encode_into_slots(gpu, kind):
     for s in (1, 2, 4):
         assert np.array_equal(after[s * bpr:(s + 1) * bpr], before[s * bpr:(s + 1) * bpr])
     assert plan.status() == 0
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_slot_array_rewritten_by_a_kernel_between_steps(gpu, kind):
+    """The kernels read the slot array through the scalar cache.  A slot array rewritten on the
+    device (a copy kernel on the same stream) between two steps must be seen by the second step:
+    the pool and readouts equal those of steps given freshly uploaded arrays."""
+    torch = gpu
+    from quantized_delta_rule_amd import stepq
+    dev = torch.device("cuda:0")
+    n_slots, first, second = 6, [0, 1, 2], [5, 3, 1]
+    wpool = _workload(kind, 128, n_slots)
+    wb = dataclasses.replace(wpool, B=len(first))
+    bits, piv, om = _plan_arrays(wpool)
+    plan = stepq.Plan(stepq.GDN if kind == "gdn" else stepq.KDA, bits, piv, om)
+    S0 = torch.from_numpy(P.warm_state(wpool, 0)).to(dev)
+    pa, pb = plan.alloc_pool(n_slots), plan.alloc_pool(n_slots)
+    plan.encode(S0, pa, n_slots)
+    plan.encode(S0, pb, n_slots)
+    g = {k: torch.from_numpy(v).to(dev) for k, v in synth.step_inputs(wb, 0, 0).items()}
+    args = (g["q"], g["k"], g["v"], g["alpha"], g["beta"])
+    B = len(first)
+    oa, ob = torch.empty((B, wb.H, wb.d), device=dev), torch.empty((B, wb.H, wb.d), device=dev)
+    reused = torch.tensor(first, dtype=torch.int32, device=dev)
+    src = torch.tensor(second, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    plan.step_slots(pa, n_slots, reused, B, *args, oa)
+    reused.copy_(src)                     # device-side rewrite between the two steps
+    plan.step_slots(pa, n_slots, reused, B, *args, oa)
+    plan.step_slots(pb, n_slots, torch.tensor(first, dtype=torch.int32, device=dev), B, *args, ob)
+    plan.step_slots(pb, n_slots, torch.tensor(second, dtype=torch.int32, device=dev), B, *args, ob)
+    torch.cuda.synchronize()
+    assert torch.equal(pa, pb) and torch.equal(oa, ob)
+    assert plan.status() == 0
