@@ -172,24 +172,30 @@ struct CodeKda<D, false> {};
 // slots: GDN column maxima pass through each wave's own (by then dead) transpose section; KDA
 // keeps them, and the rows' q, in the transpose area just past its code staging block (q is
 // dead after the readout barrier, before the transpose; the maxima come after it).
-template <int D, bool KDA>
+// RO (the split mode's readout kernels) keeps only what a readout uses -- no transpose area,
+// and for KDA the code staging block and q -- so five workgroups fit per CU.
+template <int D, bool KDA, bool RO = false>
 struct Smem {
   static constexpr int NW = Geo<D>::NW;
   static constexpr bool kKDA = KDA;
   static constexpr int NSLOT = 2;
-  Row<KDA> row[D];
-  float red[NSLOT][NW][D];
-  union {
-    float absT[NW][32][65];  // [wave][row][lane], +1 pad: conflict-free
-    CodeKda<D, KDA> kc;      // used only before and after the transpose
-  };
+  static constexpr int kSec = 32 * 65;  // one wave's transpose section [row][lane], +1 pad
   // KDA: column-maximum slots [NW][D] and the rows' q [D], after the code staging block
   static constexpr int kKdaMax = KDA ? (int)(sizeof(CodeKda<D, KDA>) / sizeof(float)) : 0;
   static constexpr int kKdaQ = kKdaMax + NW * D;
-  static_assert(!KDA || kKdaQ + D <= NW * 32 * 65, "KDA staging overflows the transpose area");
+  static constexpr int kTr = !RO ? NW * kSec : KDA ? kKdaQ + D : 1;
+  Row<KDA> row[D];
+  float red[NSLOT][NW][D];
+  union {
+    float tr[kTr];           // the waves' transpose sections (conflict-free), q, KDA maxima
+    CodeKda<D, KDA> kc;      // used only before and after the transpose
+  };
+  static_assert(!KDA || kKdaQ + D <= kTr, "KDA staging overflows the transpose area");
 };
 static_assert(sizeof(Smem<128, false>) <= 40960 && sizeof(Smem<128, true>) <= 40960,
               "four workgroups per CU need at most 40 KB of LDS each");
+static_assert(sizeof(Smem<128, false, true>) <= 32768 && sizeof(Smem<128, true, true>) <= 32768,
+              "five readout workgroups per CU need at most 32 KB of LDS each");
 
 // An integer the optimizer cannot see through: each array's row base below gets its own copy,
 // so the array's address stays in its own VGPR and each access uses the instruction's small
@@ -316,8 +322,8 @@ __device__ __forceinline__ void xwave_sum(SM& sm, int slot, int lane, float* x) 
 // once that wave's row factors are done), KDA tiles in cross-wave slot 2.
 template <int D, typename SM>
 __device__ __forceinline__ float* max_slot(SM& sm, int w) {
-  if constexpr (SM::kKDA) return &sm.absT[0][0][0] + SM::kKdaMax + w * D;
-  else return &sm.absT[w][0][0];
+  if constexpr (SM::kKDA) return sm.tr + SM::kKdaMax + w * D;
+  else return sm.tr + w * SM::kSec;
 }
 template <int D, typename SM>
 __device__ __forceinline__ void xwave_max_put(SM& sm, int w, int lane, const float* x) {
@@ -330,7 +336,7 @@ __device__ __forceinline__ void xwave_max(SM& sm, int lane, float* x) {
   constexpr int G = Geo<D>::G, NW = Geo<D>::NW;
   // wave w' partials sit at a constant distance from wave 0's
   const float* const p0 = lds_pin(sm, max_slot<D>(sm, 0) + G * lane);
-  constexpr int kStride = SM::kKDA ? D : 32 * 65;
+  constexpr int kStride = SM::kKDA ? D : SM::kSec;
   sfor<G>([&](auto gg) {
     constexpr int g = CI(gg);
     float m = p0[g];
@@ -343,7 +349,7 @@ __device__ __forceinline__ void xwave_max(SM& sm, int lane, float* x) {
 template <int D, typename SM>
 __device__ __forceinline__ void put_rowabs(SM& sm, const float (&S)[32][Geo<D>::G], int lane) {
   constexpr int G = Geo<D>::G;
-  float* const dst = lds_pin(sm, &sm.absT[0][0][0] + (threadIdx.x >> 6) * (32 * 65) + lane);
+  float* const dst = lds_pin(sm, sm.tr + (threadIdx.x >> 6) * SM::kSec + lane);
   sfor<32>([&](auto rr) {
     constexpr int r = CI(rr);
     float a;
@@ -362,7 +368,7 @@ __device__ __forceinline__ void row_factor(SM& sm, int lane, int row, float den,
                                            bool piv, uint16_t* rblk, unsigned& fl) {
   float lv[6];
   const float* const src = lds_pin(
-      sm, &sm.absT[0][0][0] + (threadIdx.x >> 6) * (32 * 65) + (lane & 31) * 65 + (lane & 32));
+      sm, sm.tr + (threadIdx.x >> 6) * SM::kSec + (lane & 31) * 65 + (lane & 32));
   sfor<32>([&](auto jj) { tree_push<CI(jj)>(lv, src[CI(jj)]); });
   const float other = __shfl_xor(lv[5], 32);
   const float m = (lane < 32 ? lv[5] + other : other + lv[5]) * (1.0f / (float)D);
@@ -547,7 +553,7 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
       const float ar = a * rf;
       rec.kr = A.P.order ? kk * ar : kk * rf;
       rec.bk = beta * kk;
-      if constexpr (KDA) (&sm.absT[0][0][0])[SM::kKdaQ + row] = qv;
+      if constexpr (KDA) sm.tr[SM::kKdaQ + row] = qv;
       else rec.q = qv;
     }
     if constexpr (MODE == WRITE) rec.bk = bk;
@@ -887,7 +893,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     });
     if constexpr (kRead) {
       float o[G];
-      const float* const qk = lds_pin(sm, &sm.absT[0][0][0] + SM::kKdaQ + row0);
+      const float* const qk = lds_pin(sm, sm.tr + SM::kKdaQ + row0);
       row_dot<G>(S, [&](int r) { return qk[r]; }, o);
       xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
@@ -904,7 +910,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     wave_lds_sync();
     const bool piv = meta_pivot(sm.row[row].meta);
     row_factor<D>(sm, lane, row, den, om, piv, rblk, fl);
-    __syncthreads();  // absT dead for every wave: the code staging area is zeroed for packing
+    __syncthreads();  // every wave's transposes are done: zero the code staging for packing
     {
       const int n4 = nwords * 16;
       u32x4* l4 = reinterpret_cast<u32x4*>(sm.kc.code);
@@ -1041,8 +1047,8 @@ __device__ __forceinline__ long long pool_slot(const StepArgs& A, int b, int h) 
 // Workgroup j runs head head_order[j / B] of request j % B: heads are dispatched in the plan's
 // order (longest tiles first, FP16 pivot heads last), which shortens the launch's ragged end.
 template <int D, int MODE>
-__global__ __launch_bounds__(Geo<D>::NT, 4) void k_gdn(StepArgs A) {
-  __shared__ Smem<D, false> sm;
+__global__ __launch_bounds__(Geo<D>::NT, MODE == READ ? 5 : 4) void k_gdn(StepArgs A) {
+  __shared__ Smem<D, false, MODE == READ> sm;
   const int hs = blockIdx.x / A.B, b = blockIdx.x - hs * A.B;
   const int h = kread(A.P.head_order, hs);
   const long long slot = pool_slot<MODE>(A, b, h);
@@ -1064,8 +1070,8 @@ __global__ __launch_bounds__(Geo<D>::NT, 4) void k_gdn(StepArgs A) {
 }
 
 template <int D, int MODE>
-__global__ __launch_bounds__(Geo<D>::NT, 4) void k_kda(StepArgs A) {
-  __shared__ Smem<D, true> sm;
+__global__ __launch_bounds__(Geo<D>::NT, MODE == READ ? 5 : 4) void k_kda(StepArgs A) {
+  __shared__ Smem<D, true, MODE == READ> sm;
   const int tile = blockIdx.x;
   const int b = tile / A.P.H, h = tile - b * A.P.H;
   const long long slot = pool_slot<MODE>(A, b, h);
