@@ -75,6 +75,10 @@ def lib() -> ctypes.CDLL:
         L.orc_encode.argtypes = [i, i, P, P, P, P, P, P, P]
         L.orc_tile_step_o.restype = i
         L.orc_tile_step_o.argtypes = [i, i, P, P, P, P, P, P, P, P, f, P, P, P, P, i]
+        L.orc_encode_dbg.restype = i
+        L.orc_encode_dbg.argtypes = [i, i, P, P, P, P, P, P, P, P, P]
+        L.orc_tile_step_dbg.restype = i
+        L.orc_tile_step_dbg.argtypes = [i, i, P, P, P, P, P, P, P, P, f, P, P, P, P, P, P, i]
         L.orc_fp32_step_o.argtypes = [i, i, P, P, P, P, P, f, P, i]
         L.orc_fp32_run_o.argtypes = [i, i, i, i, P, P, P, P, l, P, l, P, P, i]
         _lib = L
@@ -184,6 +188,42 @@ class Head:
         if want_state:
             return out, S.reshape(self.dk, self.dv), pre.reshape(self.dk, self.dv), fl.value
         return out
+
+
+    def encode_dbg(self, S):
+        """encode() with every intermediate the packed state does not show: returns
+        (seg, dict(pre, z0, c0, flags)) -- pre the final pre-rounding values, z0 the first codes,
+        c0 the first column factors."""
+        S = _c(S, np.float32)
+        seg = np.zeros(self.seg_bytes, np.uint8)
+        pre = np.empty(self.dk * self.dv, np.float64)
+        z0 = np.empty(self.dk * self.dv, np.int8)
+        c0 = np.empty(self.dv, np.float32)
+        fl = ctypes.c_uint32(0)
+        lib().orc_encode_dbg(self.dk, self.dv, _p(self.bits), _p(self.pivot), _p(self.omega),
+                             _p(S), _p(seg), _p(pre), _p(z0), _p(c0), ctypes.addressof(fl))
+        return seg, dict(pre=pre.reshape(self.dk, self.dv), z0=z0.reshape(self.dk, self.dv),
+                         c0=c0, flags=fl.value)
+
+    def step_dbg(self, seg, q, k, v, a, beta):
+        """step() in place on seg, returning dict(out, S (updated binary32 state), pre, z0, c0,
+        flags)."""
+        q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+        a = _c(np.broadcast_to(np.asarray(a, np.float32), (self.dk,)), np.float32)
+        out = np.empty(self.dv, np.float32)
+        S = np.empty(self.dk * self.dv, np.float32)
+        pre = np.empty(self.dk * self.dv, np.float64)
+        z0 = np.empty(self.dk * self.dv, np.int8)
+        c0 = np.empty(self.dv, np.float32)
+        fl = ctypes.c_uint32(0)
+        rc = lib().orc_tile_step_dbg(self.dk, self.dv, _p(self.bits), _p(self.pivot),
+                                     _p(self.omega), _p(seg), _p(q), _p(k), _p(v), _p(a),
+                                     float(beta), _p(out), _p(S), _p(pre), _p(z0), _p(c0),
+                                     ctypes.addressof(fl), self.order)
+        if rc != 0:
+            raise ValueError("corrupt code (-2^(b-1)) in segment")
+        return dict(out=out, S=S.reshape(self.dk, self.dv), pre=pre.reshape(self.dk, self.dv),
+                    z0=z0.reshape(self.dk, self.dv), c0=c0, flags=fl.value)
 
 
 def fp32_step(S, q, k, v, a, beta, order=DELTA_FIRST):

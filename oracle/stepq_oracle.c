@@ -272,8 +272,11 @@ void orc_row_den(int dk, const float* omega, float* den) {
 /* Encode the fp32 state S (dk x dv row-major) into seg.  pre (optional, dk*dv) receives the
    final pre-rounding value y_ij * (1/c_j) (exact, binary64) of every quantized entry (0
    elsewhere). */
-int orc_encode(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const float* omega,
-               const float* S, uint8_t* seg, double* pre, uint32_t* flags) {
+/* The same with the first quantization exposed: z0_out (optional, dk*dv) receives the first
+   codes z0 (0 on pivot and dead rows), c0_out (optional, dv) the first column factors c0. */
+int orc_encode_dbg(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const float* omega,
+                   const float* S, uint8_t* seg, double* pre, int8_t* z0_out, float* c0_out,
+                   uint32_t* flags) {
   seg_layout s = layout_of(dk, dv, bits, pivot);
   uint32_t fl = 0;
   float* den = (float*)malloc(sizeof(float) * dk);
@@ -316,7 +319,11 @@ int orc_encode(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const f
     ir[i] = rcp0(rr); /* a row whose factor rounds to zero is dead: all its codes are 0 */
     W[i] = (omega[i] * rr) * rr;
   }
-  if (s.allpiv) goto done;
+  if (s.allpiv) {
+    if (z0_out) memset(z0_out, 0, (size_t)dk * dv);
+    if (c0_out) memset(c0_out, 0, sizeof(float) * dv);
+    goto done;
+  }
 
   /* y = S / r (as a multiply by the rounded reciprocal); c0_j = max_i |y_ij| / qmax_i */
   for (int j = 0; j < dv; j++) {
@@ -328,6 +335,7 @@ int orc_encode(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const f
       if (t > mx) mx = t;
     }
     c0[j] = mx;
+    if (c0_out) c0_out[j] = mx;
   }
   /* first quantization with c0 (its clamp never binds: |y| / qmax <= c0), then the
      omega-weighted least-squares column refit:
@@ -338,6 +346,8 @@ int orc_encode(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const f
     for (int i = 0; i < dk; i++) {
       long e = (long)i * dv + j;
       z0[e] = (float)clampd(rne_prod(y[e], ic0), -qmax[i], qmax[i]);
+      /* NaN only follows a non-finite state (flagged); its debug copy reads 0 */
+      if (z0_out) z0_out[e] = z0[e] == z0[e] ? (int8_t)z0[e] : 0;
       a[e] = W[i] * z0[e];
     }
     float num = dot_fixed(a + j, dv, y + j, dv, dk);
@@ -368,6 +378,11 @@ done:
   free(y); free(z0); free(a); free(c0); free(ic);
   if (flags) *flags |= fl;
   return 0;
+}
+
+int orc_encode(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const float* omega,
+               const float* S, uint8_t* seg, double* pre, uint32_t* flags) {
+  return orc_encode_dbg(dk, dv, bits, pivot, omega, S, seg, pre, NULL, NULL, flags);
 }
 
 /* ------------------------------------------------------------------------------------------ */
@@ -437,19 +452,27 @@ static int decode_factored(int dk, int dv, const int8_t* bits, const uint8_t* pi
 /* Decode step of one (request, head) tile, in place on seg.  a has dk entries (all equal for
    GDN).  S_upd (optional) receives the updated fp32 state before requantization, pre (optional)
    the final pre-rounding values.  Returns 0, or -1 on a corrupt code. */
-int orc_tile_step_o(int dk, int dv, const int8_t* bits, const uint8_t* pivot,
-                    const float* omega, uint8_t* seg, const float* q, const float* k,
-                    const float* v, const float* a, float beta, float* out, float* S_upd,
-                    double* pre, uint32_t* flags, int order) {
+int orc_tile_step_dbg(int dk, int dv, const int8_t* bits, const uint8_t* pivot,
+                      const float* omega, uint8_t* seg, const float* q, const float* k,
+                      const float* v, const float* a, float beta, float* out, float* S_upd,
+                      double* pre, int8_t* z0_out, float* c0_out, uint32_t* flags, int order) {
   float* S = (float*)malloc(sizeof(float) * dk * dv);
   float* f = (float*)malloc(sizeof(float) * dk);
   int rc = decode_factored(dk, dv, bits, pivot, seg, S, f);
   delta_update_readout(dk, dv, S, f, q, k, v, a, beta, out, order);
   free(f);
   if (S_upd) memcpy(S_upd, S, sizeof(float) * dk * dv);
-  orc_encode(dk, dv, bits, pivot, omega, S, seg, pre, flags);
+  orc_encode_dbg(dk, dv, bits, pivot, omega, S, seg, pre, z0_out, c0_out, flags);
   free(S);
   return rc;
+}
+
+int orc_tile_step_o(int dk, int dv, const int8_t* bits, const uint8_t* pivot,
+                    const float* omega, uint8_t* seg, const float* q, const float* k,
+                    const float* v, const float* a, float beta, float* out, float* S_upd,
+                    double* pre, uint32_t* flags, int order) {
+  return orc_tile_step_dbg(dk, dv, bits, pivot, omega, seg, q, k, v, a, beta, out, S_upd, pre,
+                           NULL, NULL, flags, order);
 }
 
 int orc_tile_step(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const float* omega,

@@ -1,10 +1,12 @@
 """Parity at the full sizes of the five synthetic workloads, in the launch configuration the
-benchmark uses (one launch per layer and step over every tile).  The GPU runs every tile; the
-oracle follows a sample of tiles (every head at least once) through every step.
+benchmark uses (one launch per layer and step over every tile).  The GPU runs every tile through
+every step; the oracle follows a sample of tiles (every head at least once) through every step,
+bit for bit, and a few of them also against the plain binary64 reference.
 
-Workload 5 (12 layers x 256 requests x 48 heads, split mode) runs 6 decode steps instead of
-128 to keep host-side input generation within the test budget; every other workload runs all
-of its steps."""
+Workload 5 (12 layers x 256 requests x 48 heads, split mode, 128 steps): the oracle follows four
+heads per layer (head h in layer h mod 12, so every head index in some layer) plus two random
+tiles per layer, one of each layer's tiles against the plain reference each step, and layer 0
+also runs a fused plan on the same inputs that must equal the split result bit for bit."""
 import numpy as np
 import pytest
 
@@ -32,17 +34,28 @@ def test_full_size_workload(gpu, wid):
     tiles = P.sample_tiles(w, per_head=1, extra=8, seed=wid)
     P.log(f"[parity] workload {wid}: {len(tiles)} sampled tiles, running")
     tr, plan, _ = P.run_layer(w, 0, bits[0], piv[0], om[0], w.steps, tiles=tiles)
-    P.log(f"[parity] workload {wid} ok: {tr.steps} steps, boundary mismatches {tr.boundary}, "
-          f"worst readout {tr.worst_readout:.2e}")
+    P.log(f"[parity] workload {wid} ok: {tr.summary()}")
+    assert tr.steps == w.steps and tr.plain.steps > 0
     assert plan.status() == 0
+
+
+def _stress_tiles(w, layer):
+    """Head h (h = layer mod 12) with request (5 h + 3 layer) mod B, plus two random tiles."""
+    g = np.random.default_rng(100 + layer)
+    tl = [((5 * h + 3 * layer) % w.B) * w.H + h for h in range(layer % w.layers, w.H, w.layers)]
+    tl += [int(t) for t in g.choice(w.B * w.H, 2, replace=False)]
+    return sorted(set(tl))
 
 
 def test_full_size_workload_5_split(gpu):
     w = synth.WORKLOADS[5]
     P.log(f"[parity] workload 5 {w.name}: {w.layers} layers x B={w.B} x H={w.H}: plan")
-    plans_np = P.oracle_plan(w)
-    tl = lambda l: P.sample_tiles(w, per_head=0, extra=6, seed=100 + l)
-    tr, plans = P.run_layers_split(w, plans_np, 6, tl)
+    plans_np, S0s = P.split_setup(w)
+    covered = {t % w.H for l in range(w.layers) for t in _stress_tiles(w, l)}
+    assert covered == set(range(w.H))
+    tr, plans = P.run_layers_split(w, plans_np, w.steps, lambda l: _stress_tiles(w, l), S0s=S0s)
+    P.log(f"[parity] workload 5 ok: {tr.summary()}")
+    assert tr.steps == w.steps and tr.plain.steps == w.steps * w.layers
     assert all(p.status() == 0 for p in plans)
 
 
