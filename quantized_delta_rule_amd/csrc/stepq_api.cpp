@@ -17,9 +17,11 @@
 
 using namespace stepq;
 
-namespace {
+namespace stepq {
 
+namespace {
 thread_local std::string g_err;
+}  // namespace
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -31,8 +33,16 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+void clear_error() { g_err.clear(); }
+
+const char* last_error() { return g_err.c_str(); }
+
+}  // namespace stepq
+
+namespace {
+
 int ok() {
-  g_err.clear();
+  clear_error();
   return STEPQ_OK;
 }
 
@@ -128,7 +138,7 @@ int refuse_capture(stepq_plan* p, hipStream_t stream, const char* what) {
 
 extern "C" {
 
-const char* stepq_last_error(void) { return g_err.c_str(); }
+const char* stepq_last_error(void) { return stepq::last_error(); }
 
 int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   if (!d || !out) return fail(STEPQ_ERR_INVALID_ARG, "desc and out must be non-NULL");

@@ -1,5 +1,6 @@
-// stepq_internal.h -- shared between the host API (stepq_api.cpp) and the kernels
-// (stepq_kernels.hip).  Not part of the public ABI.
+// stepq_internal.h -- shared between the host API (stepq_api.cpp, stepq_offline.cpp) and the
+// kernels (stepq_device.h, instantiated by stepq_k128_gdn.hip, stepq_k128_kda.hip and
+// stepq_k64.hip).  Not part of the public ABI.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -59,7 +60,7 @@ struct StepArgs {
   int* slot_out;
 };
 
-// Launchers (stepq_kernels.hip).  kind: 0 = GDN, 1 = KDA.
+// Launchers (stepq_k64.hip; stepq_calib.hip for the row impact).  kind: 0 = GDN, 1 = KDA.
 hipError_t launch_step(int kind, Mode mode, const StepArgs& a, hipStream_t s);
 hipError_t launch_unpack(const DevPlan& P, const uint8_t* pool, int B, float* S, uint16_t* r,
                          uint16_t* c, int8_t* z, hipStream_t s);
@@ -67,5 +68,10 @@ hipError_t launch_row_impact(int kind, int order, int H, int D, int B, const flo
                              const float* k, const float* alpha, const float* beta, double* acc,
                              hipStream_t s);
 hipError_t launch_spin(long long cycles, hipStream_t s);
+
+// The calling thread's message of the last call (stepq_last_error): fail() records a printf-style
+// message and returns code; clear_error() empties it.  Shared by every host entry point.
+int fail(int code, const char* fmt, ...);
+void clear_error();
 
 }  // namespace stepq

@@ -17,13 +17,11 @@
 #include <vector>
 
 #include "stepq.h"
+#include "stepq_internal.h"
 
 namespace {
-thread_local std::string g_off_err;
-int bad(const char* m) {
-  g_off_err = m;
-  return STEPQ_ERR_INVALID_ARG;
-}
+// a refused call: its message goes to the library's error slot (stepq_last_error)
+int bad(const char* m) { return stepq::fail(STEPQ_ERR_INVALID_ARG, "%s", m); }
 }  // namespace
 
 extern "C" {
@@ -36,6 +34,7 @@ int stepq_lifetime_weights(const double* l_u, int n, int H, double* L_out) {
     // geometric series sum_{j<H} x^j with x = exp(2l), written with expm1 so l -> 0 stays exact
     L_out[u] = l == 0.0 ? (double)H : std::expm1(2.0 * H * l) / std::expm1(2.0 * l);
   }
+  stepq::clear_error();
   return STEPQ_OK;
 }
 
@@ -63,6 +62,7 @@ int stepq_row_impact_accumulate(int n, int d, const float* q, const float* k, co
       acc[i] += g * g;
     }
   }
+  stepq::clear_error();
   return STEPQ_OK;
 }
 
@@ -75,6 +75,7 @@ int stepq_select_pivots(const double* risk, int n, int n_pivots, int32_t* out_id
   std::vector<int> pick(idx.begin(), idx.begin() + n_pivots);
   std::sort(pick.begin(), pick.end());
   for (int i = 0; i < n_pivots; i++) out_idx[i] = pick[i];
+  stepq::clear_error();
   return STEPQ_OK;
 }
 
@@ -123,6 +124,7 @@ int stepq_alloc_mcdp(const double* cost, int n_units, const int* choices, int n_
     c -= choices[ci] / 2;
   }
   if (objective) *objective = best;
+  stepq::clear_error();
   return STEPQ_OK;
 }
 
@@ -195,6 +197,7 @@ int stepq_alloc_lagrangian(const double* L, const double* d, const double* n, in
     obj += L[u] * d[(size_t)u * n_choices + bi[u]];
   }
   if (objective) *objective = obj;
+  stepq::clear_error();
   return STEPQ_OK;
 }
 

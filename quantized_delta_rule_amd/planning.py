@@ -26,8 +26,7 @@ def omega(w: synth.Workload, layer: int, phase: str | None = None, steps: int | 
     steps = dsteps if steps is None else steps
     acc = np.zeros((w.H, w.d))
     n = 0
-    for s in range(steps):
-        x = synth.step_inputs(w, layer, s, phase)
+    for x in synth.step_inputs_many(w, layer, range(steps), phase):
         a = synth.alpha_rows(w, x["alpha"])
         for h in range(w.H):
             stepq.row_impact_accumulate(x["q"][:, h], x["k"][:, h], a[:, h], x["beta"][:, h],

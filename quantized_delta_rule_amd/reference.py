@@ -36,12 +36,15 @@ def device_inputs(x, w: synth.Workload, dev, n_req=None):
             "beta": t(x["beta"][sl].reshape(-1)), "alpha": t(x["alpha"][sl])}
 
 
-def warm_state(w: synth.Workload, layer: int, dev):
-    """Initial states [B*H, d, d]: w.warmup steps from zero on the warm-up stream."""
+def warm_state(w: synth.Workload, layer: int, dev, xs=None):
+    """Initial states [B*H, d, d]: w.warmup steps from zero on the warm-up stream (xs: those
+    steps' inputs if already drawn)."""
     import torch
     S = torch.zeros((w.B * w.H, w.d, w.d), dtype=torch.float32, device=dev)
-    for s in range(w.warmup):
-        x = device_inputs(synth.step_inputs(w, layer, s, "warmup"), w, dev)
+    if xs is None:
+        xs = synth.step_inputs_many(w, layer, range(w.warmup), "warmup")
+    for x_ in xs:
+        x = device_inputs(x_, w, dev)
         fp32_step(S, x["q"], x["k"], x["v"], x["a"], x["beta"])
     return S
 

@@ -150,6 +150,17 @@ def step_inputs(w: Workload, layer: int, step: int, phase: str = "decode"):
     return dict(q=f(q), k=f(k), v=f(v), alpha=f(alpha), beta=f(beta))
 
 
+def step_inputs_many(w: Workload, layer: int, steps, phase: str = "decode", workers: int = 8):
+    """step_inputs for each of `steps`, drawn on a thread pool.  Each (layer, step) has its own
+    seeded stream, so the result does not depend on the number of workers."""
+    from concurrent.futures import ThreadPoolExecutor
+    steps = list(steps)
+    if workers <= 1 or len(steps) <= 1:
+        return [step_inputs(w, layer, s, phase) for s in steps]
+    with ThreadPoolExecutor(min(workers, len(steps))) as ex:
+        return list(ex.map(lambda s: step_inputs(w, layer, s, phase), steps))
+
+
 def alpha_rows(w: Workload, alpha):
     """Per-row gate a_i of every tile: GDN broadcasts the scalar gate over the d_k rows."""
     alpha = np.asarray(alpha, np.float32)

@@ -145,3 +145,30 @@ def test_lagrangian_matches_oracle(sq, orc, seed):
     b2, o2 = orc.lagrangian_allocate(L, d, n, choices, 6 * n.sum())
     assert o1 == pytest.approx(o2, rel=1e-12)
     assert np.array_equal(b1, b2)
+
+
+def test_refused_planner_calls_report_their_own_message(sq):
+    """A refused host planner call leaves its message in stepq_last_error (the one error slot
+    of the library), and a successful call clears it."""
+    L = sq.lib()
+    cost = np.ones((3, 2))
+    ch = np.array([4, 6], np.int32)
+    out = np.zeros(3, np.int32)
+    obj = ctypes.c_double()
+    rc = L.stepq_alloc_mcdp(cost.ctypes.data, 3, ch.ctypes.data, 2, 2, out.ctypes.data,
+                            ctypes.byref(obj))
+    assert rc == -1 and "alloc_mcdp: budget below the narrowest width" in \
+        L.stepq_last_error().decode()
+    bad_ch = np.array([6, 4], np.int32)
+    rc = L.stepq_alloc_mcdp(cost.ctypes.data, 3, bad_ch.ctypes.data, 2, 30, out.ctypes.data,
+                            ctypes.byref(obj))
+    assert rc == -1 and "ascending" in L.stepq_last_error().decode()
+    l_u = np.array([0.5])
+    Lw = np.zeros(1)
+    assert L.stepq_lifetime_weights(l_u.ctypes.data, 1, 8, Lw.ctypes.data) == -1
+    assert "l_u must be finite and <= 0" in L.stepq_last_error().decode()
+    l_u[0] = -0.1
+    assert L.stepq_lifetime_weights(l_u.ctypes.data, 1, 8, Lw.ctypes.data) == 0
+    assert L.stepq_last_error().decode() == ""
+    with pytest.raises(sq.StepqError, match="budget below"):
+        sq.alloc_mcdp(cost, [4, 6], 2)

@@ -189,3 +189,20 @@ def test_status_flags_match_oracle(torch_gpu):
     P.log(f"[parity] step flags gpu {got} oracle {want}")
     assert want & stepq.FLAG_NONFINITE
     assert got == want
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_uniform_width_unit_impact_plan(torch_gpu, kind):
+    """The baseline plan of the ablation (every unit at one width, no pivots, omega = 1, so every
+    row's denominator is 1 + 1 = 2 and the refit weights rows evenly) through the same kernels,
+    checked against the oracle and the plain reference like the STEPQuant plans."""
+    w = dataclasses.replace(synth.WORKLOADS[2], wid=420 + (kind == "kda"), kind=kind, B=6,
+                            steps=12, alloc="fixed", n_pivots=0)
+    P.log(f"[parity] uniform-6, omega = 1, {kind}: B={w.B} H={w.H}")
+    bits = np.full((w.H, w.d), 6, np.int8)
+    piv = np.zeros((w.H, w.d), np.uint8)
+    om = np.ones((w.H, w.d), np.float32)
+    tr, plan, _ = P.run_layer(w, 0, bits, piv, om, w.steps,
+                              tiles=P.sample_tiles(w, per_head=1, extra=4, seed=42))
+    P.log(f"[parity] uniform-6 {kind} ok: {tr.summary()}")
+    assert plan.status() == 0 and tr.plain.steps > 0
