@@ -156,6 +156,28 @@ int stepq_decode_step_slots(stepq_plan_t plan, void* pool, int n_slots, const in
 int stepq_encode_state_slots(stepq_plan_t plan, const float* S, void* pool, int n_slots,
                              const int32_t* slots, int B, void* stream);
 
+/*
+ * stepq_decode_step without any device allocation, for callers that cannot allocate: code that
+ * must not call hipMalloc (tight serving loops, harnesses that forbid allocation).  Arguments,
+ * layout, results and stream ordering are those of stepq_decode_step; the results are
+ * bit-identical to it.
+ *   Fused plan: the same kernel as stepq_decode_step (it uses no scratch memory).
+ *   Split plan: the readout kernel hands its per-tile update factors to the side-stream
+ *   writeback through a library-static device array of 32 MiB per GPU (held from the plan's
+ *   creation until the process ends) instead of the plan's own buffer; B may exceed the plan's
+ *   max_batch up to that array's size: B * n_heads * d_k * 16 bytes <= 32 MiB (16384 tiles at
+ *   d_k = 128, 32768 at 64).  Larger B: STEPQ_ERR_INVALID_ARG, nothing enqueued.
+ * Every split plan on one GPU shares that GPU's array, which keeps the last call's contents.  A
+ * call waits (on `stream`) for the previous call's writeback on the same GPU before its readout
+ * overwrites the array, so calls issued one after another from one host thread are ordered;
+ * calls issued concurrently from several host threads on one GPU race.  The call allocates
+ * nothing: no hipMalloc, hipFree or allocating library routine (the array's device address is
+ * resolved once per GPU when a split plan is created there).
+ */
+int stepq_decode_step_noalloc(stepq_plan_t plan, void* pool, int B, const float* q,
+                              const float* k, const float* v, const float* alpha,
+                              const float* beta, float* out, void* stream);
+
 /* Debug decode of a pool: S_hat [B, n_heads, d_k, d_v] = r_i c_j z_ij (pivots as stored),
    r [B, n_heads, d_k] and c [B, n_heads, d_v] binary16 bit patterns, z [B, n_heads, d_k, d_v]
    codes (0 on pivot rows).  Any output may be NULL. */

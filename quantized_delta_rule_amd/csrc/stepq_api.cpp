@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -87,7 +88,16 @@ struct stepq_plan {
   hipEvent_t ev_read = nullptr, ev_write = nullptr;
   bool write_pending = false;
   long long spin_cycles = 0;
+  void* scratch = nullptr;   // split mode: this device's scratch array (no-allocation entry)
 };
+
+namespace {
+// Per device, the split plan whose side-stream writeback last read the device scratch through
+// stepq_decode_step_noalloc: the next such call waits for that writeback before its readout
+// kernel overwrites the hand-over.
+std::mutex g_scratch_mu;
+stepq_plan* g_scratch_owner[64] = {};
+}  // namespace
 
 namespace {
 
@@ -99,6 +109,11 @@ int check_plan(stepq_plan_t p) {
 void destroy_plan(stepq_plan* p) {
   if (!p) return;
   if (p->side) (void)hipStreamSynchronize(p->side);
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (p->device >= 0 && p->device < 64 && g_scratch_owner[p->device] == p)
+      g_scratch_owner[p->device] = nullptr;
+  }
   if (p->ev_read) (void)hipEventDestroy(p->ev_read);
   if (p->ev_write) (void)hipEventDestroy(p->ev_write);
   if (p->side) (void)hipStreamDestroy(p->side);
@@ -326,6 +341,10 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
       return fail(STEPQ_ERR_OOM, "hipMalloc(%zu) for the split-mode hand-over: %s", n,
                   hipGetErrorString(e));
     }
+    if (int rc = scratch_resolve(d->device, &p->scratch)) {
+      destroy_plan(p);
+      return rc;
+    }
     if ((e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&p->ev_read, hipEventDisableTiming)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&p->ev_write, hipEventDisableTiming)) != hipSuccess) {
@@ -400,11 +419,11 @@ int encode_impl(stepq_plan_t p, const float* S, void* pool, int n_slots, const i
 
 int decode_impl(stepq_plan_t p, void* pool, int n_slots, const int32_t* slots, int B,
                 const float* q, const float* k, const float* v, const float* alpha,
-                const float* beta, float* out, void* stream) {
+                const float* beta, float* out, void* stream, float* stash = nullptr) {
   if (B > 0 && (!q || !k || !v || !alpha || !beta || !out))
     return fail(STEPQ_ERR_INVALID_ARG, "q, k, v, alpha, beta and out must be non-NULL");
   if (int rc = check_grid(p, B)) return rc;
-  if (p->mode == STEPQ_MODE_SPLIT && B > p->max_batch)
+  if (p->mode == STEPQ_MODE_SPLIT && !stash && B > p->max_batch)
     return fail(STEPQ_ERR_INVALID_ARG, "B = %d exceeds max_batch %d", B, p->max_batch);
   if (B == 0) return ok();
   DeviceGuard dg(p->device);
@@ -420,7 +439,7 @@ int decode_impl(stepq_plan_t p, void* pool, int n_slots, const int32_t* slots, i
   a.alpha = alpha;
   a.beta = beta;
   a.out = out;
-  a.stash = p->stash;
+  a.stash = stash ? stash : p->stash;
   a.slots = slots;
   a.n_slots = n_slots;
   if (p->mode == STEPQ_MODE_FUSED) {
@@ -472,6 +491,36 @@ int stepq_decode_step_slots(stepq_plan_t p, void* pool, int n_slots, const int32
   if (int rc = check_plan(p)) return rc;
   if (int rc = check_slots(pool, n_slots, slots, B)) return rc;
   return decode_impl(p, pool, n_slots, slots, B, q, k, v, alpha, beta, out, stream);
+}
+
+int stepq_decode_step_noalloc(stepq_plan_t p, void* pool, int B, const float* q,
+                              const float* k, const float* v, const float* alpha,
+                              const float* beta, float* out, void* stream) {
+  if (int rc = check_plan(p)) return rc;
+  if (int rc = check_pool(pool, B)) return rc;
+  if (p->mode == STEPQ_MODE_FUSED)  // the fused kernel uses no scratch: the plain call
+    return decode_impl(p, pool, B, nullptr, B, q, k, v, alpha, beta, out, stream);
+  const size_t need = (size_t)B * p->H * 4 * p->D * sizeof(float);
+  if (need > kScratchBytes)
+    return fail(STEPQ_ERR_INVALID_ARG, "decode_step_noalloc: B * n_heads = %lld tiles need %zu "
+                "bytes of scratch, above its %zu (at most %zu tiles at d = %d)",
+                (long long)B * p->H, need, kScratchBytes, kScratchBytes / (16 * (size_t)p->D),
+                p->D);
+  if (B == 0) return ok();
+  if (!p->scratch) return fail(STEPQ_ERR_HIP, "decode_step_noalloc: scratch not resolved");
+  // the previous no-allocation writeback on this device (another plan's) must have read the
+  // hand-over before this readout kernel overwrites it; this plan's own is waited for below
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    stepq_plan* prev = g_scratch_owner[p->device];
+    if (prev && prev != p && prev->write_pending) {
+      DeviceGuard dg(p->device);
+      HIP_TRY(hipStreamWaitEvent((hipStream_t)stream, prev->ev_write, 0));
+    }
+    g_scratch_owner[p->device] = p;
+  }
+  return decode_impl(p, pool, B, nullptr, B, q, k, v, alpha, beta, out, stream,
+                     (float*)p->scratch);
 }
 
 int stepq_unpack_debug(stepq_plan_t p, const void* pool, int B, float* S_hat, uint16_t* r,

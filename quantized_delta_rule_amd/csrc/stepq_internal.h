@@ -69,6 +69,11 @@ hipError_t launch_row_impact(int kind, int order, int H, int D, int B, const flo
                              hipStream_t s);
 hipError_t launch_spin(long long cycles, hipStream_t s);
 
+// The no-allocation entry point's device scratch (stepq_noalloc.hip): kScratchBytes per GPU,
+// resolved once per device; the current device must be `device`.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+int scratch_resolve(int device, void** out);
+
 // The calling thread's message of the last call (stepq_last_error): fail() records a printf-style
 // message and returns code; clear_error() empties it.  Shared by every host entry point.
 int fail(int code, const char* fmt, ...);

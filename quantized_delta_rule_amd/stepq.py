@@ -52,6 +52,7 @@ def lib() -> ctypes.CDLL:
         "stepq_head_segment": (i, [P, i, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
         "stepq_encode_state": (i, [P, P, P, i, P]),
         "stepq_decode_step": (i, [P, P, i, P, P, P, P, P, P, P]),
+        "stepq_decode_step_noalloc": (i, [P, P, i, P, P, P, P, P, P, P]),
         "stepq_encode_state_slots": (i, [P, P, P, i, P, i, P]),
         "stepq_decode_step_slots": (i, [P, P, i, P, i, P, P, P, P, P, P, P]),
         "stepq_unpack_debug": (i, [P, P, i, P, P, P, P, P]),
@@ -190,6 +191,16 @@ class Plan:
         args = self._step_args(B, q, k, v, alpha, beta, out)
         _check(lib().stepq_decode_step(self._h, self._pool(pool, B), int(B), *args,
                                        _stream_ptr(stream)), "decode_step")
+
+    def step_noalloc(self, pool, B, q, k, v, alpha, beta, out, stream=None):
+        """stepq_decode_step_noalloc: the same step with no device allocation (split plans
+        hand over through the library's static device scratch; B may exceed max_batch up to
+        that scratch's size)."""
+        if B < 0:
+            raise ValueError("B must be >= 0")
+        args = self._step_args(B, q, k, v, alpha, beta, out)
+        _check(lib().stepq_decode_step_noalloc(self._h, self._pool(pool, B), int(B), *args,
+                                               _stream_ptr(stream)), "decode_step_noalloc")
 
     # -- slot-indexed pools: batch row b uses pool slot slots[b] (-1 = padding row) --------
     def _slots(self, slots, B):
