@@ -16,22 +16,33 @@
  *     fit over value columns with r fixed; z are low-bit integers stored per the offline map.
  *   - Method 4, "the execution path of each decode step": reconstruct from codes, scales and FP16
  *     pivots; retention + delta update + readout on the float tile; the output leaves before
- *     requantization; refit r and c; pack codes and scales with pivots kept in FP16.  The row
- *     factor of the reconstruction enters the update through the row coefficients k_i r_i and
- *     a_i r_i (same product, one rounding fewer per entry than forming r_i c_j z_ij first).
+ *     requantization; refit r and c; pack codes and scales with pivots kept in FP16.
  * The scale formulas (r_i = (mean_j|S_ij| + 1e-8)/(1 + omega_i/mean omega), c_j initialised to
  * max_i|S_ij/r_i|/qmax, one omega-weighted least-squares refit with z fixed, symmetric
  * round-half-even with qmax = 2^(b-1)-1) and the gate A_t = Diag(a)(I - beta k k^T) are the
  * readings this build takes where the pages leave the step open; the other gate order,
  * A_t = (I - beta k k^T) Diag(a), is available as a plan option (ORC_DECAY_FIRST).
  *
+ * This is one binary32 evaluation order of that step, fixed so that a GPU can follow it bit for
+ * bit; oracle/plain.py states the step in binary64 without it, and the tests check this file
+ * against that statement within the binary32 error bounds.  The order's choices:
+ *   - the stored state is a row factor f_i (r_hat_i, or 1 on FP16 pivot rows) times
+ *     X_ij = c_j z_ij (exact) or the pivot value;
+ *   - the updated state is kept as S_ij = M_i T_ij with T_ij = fma(K_i, e_ij, X_ij),
+ *     M_i = a_i f_i and K_i = (beta k_i) / M_i, which is a_i f_i X_ij + beta k_i e_ij;
+ *     a row whose gate is below 2^-72 in magnitude (its previous state is erased) takes
+ *     X_ij := 0, and such a row or one with f_i = 0 takes M_i = beta k_i, K_i = 1;
+ *   - every later per-row scale (readout coefficient q_i M_i, row magnitude |M_i|, the scaled
+ *     state y = T (M_i / r_hat_i)) is one per-row product;
+ *   - r_i = (mean + 1e-8) * (1 / den_i) with the reciprocal taken once per plan;
+ *   - codes round the exact product y * (1/c) once (no intermediate rounding of the product).
  * Arithmetic: IEEE binary32, round to nearest even, subnormals kept.  Every operation is rounded
- * on its own; a fused multiply-add appears only where fmaf() is written.  A code is the
- * round-half-even integer of the exact product y * (1/c) (no intermediate rounding of the
- * product).  Build with -ffp-contract=off and without -ffast-math.  Sums run in a fixed order:
+ * on its own; a fused multiply-add appears only where fmaf() is written.  Build with
+ * -ffp-contract=off and without -ffast-math.  Sums run in a fixed order:
  *   tree(x_0..x_{n-1})  pairwise: tree(first half) + tree(second half); tree(x) = x.
- *   dot(x, y)           aligned groups of four terms are accumulated first to last with
- *                       fused multiply-adds, and the group sums are combined by tree().
+ *   dot(x, y)           consecutive blocks of 32 terms are each accumulated first to last with
+ *                       fused multiply-adds (the first term a rounded product), and the block
+ *                       sums are combined by tree().
  * The two fixed orders make CPU and GPU results comparable bit for bit.
  */
 #include <math.h>
@@ -98,18 +109,20 @@ static float tree_sum(const float* x, int n) {
   return tree_sum(x, n / 2) + tree_sum(x + n / 2, n - n / 2);
 }
 
-/* dot over n terms (n a multiple of 4 and n/4 a power of two); x[i*xs], y[i*ys] */
+#define ORC_BLOCK 32      /* rows of one fma chain in dot() */
+
+/* dot over n >= 1 terms, x[i*xs], y[i*ys]: blocks of 32 consecutive terms (the last one
+   shorter if 32 does not divide n), at most 16 blocks */
 static float dot_fixed(const float* x, int xs, const float* y, int ys, int n) {
-  float quad[64];
-  for (int m = 0; m < n / 4; m++) {
-    int i = 4 * m;
-    float s = x[i * xs] * y[i * ys];
-    s = fmaf(x[(i + 1) * xs], y[(i + 1) * ys], s);
-    s = fmaf(x[(i + 2) * xs], y[(i + 2) * ys], s);
-    s = fmaf(x[(i + 3) * xs], y[(i + 3) * ys], s);
-    quad[m] = s;
+  float blk[16];
+  int nb = (n + ORC_BLOCK - 1) / ORC_BLOCK;
+  for (int m = 0; m < nb; m++) {
+    int i0 = ORC_BLOCK * m, i1 = i0 + ORC_BLOCK < n ? i0 + ORC_BLOCK : n;
+    float s = x[i0 * xs] * y[i0 * ys];
+    for (int i = i0 + 1; i < i1; i++) s = fmaf(x[i * xs], y[i * ys], s);
+    blk[m] = s;
   }
-  return tree_sum(quad, n / 4);
+  return tree_sum(blk, nb);
 }
 
 float orc_tree_sum(const float* x, int n) { return tree_sum(x, n); }
@@ -269,14 +282,13 @@ void orc_row_den(int dk, const float* omega, float* den) {
   for (int i = 0; i < dk; i++) den[i] = mean > 0.0f ? 1.0f + omega[i] / mean : 1.0f;
 }
 
-/* Encode the fp32 state S (dk x dv row-major) into seg.  pre (optional, dk*dv) receives the
-   final pre-rounding value y_ij * (1/c_j) (exact, binary64) of every quantized entry (0
-   elsewhere). */
-/* The same with the first quantization exposed: z0_out (optional, dk*dv) receives the first
-   codes z0 (0 on pivot and dead rows), c0_out (optional, dv) the first column factors c0. */
-int orc_encode_dbg(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const float* omega,
-                   const float* S, uint8_t* seg, double* pre, int8_t* z0_out, float* c0_out,
-                   uint32_t* flags) {
+/* Requantize the state S_ij = M_i T_ij (dk x dv row-major T, per-row M) into seg.
+   pre (optional, dk*dv) receives the final pre-rounding value y_ij * (1/c_j) (exact, binary64)
+   of every quantized entry (0 elsewhere), z0_out (optional, dk*dv) the first codes (0 on pivot
+   and dead rows), c0_out (optional, dv) the first column factors. */
+static int requant(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const float* omega,
+                   const float* T, const float* M, uint8_t* seg, double* pre, int8_t* z0_out,
+                   float* c0_out, uint32_t* flags) {
   seg_layout s = layout_of(dk, dv, bits, pivot);
   uint32_t fl = 0;
   float* den = (float*)malloc(sizeof(float) * dk);
@@ -293,17 +305,18 @@ int orc_encode_dbg(int dk, int dv, const int8_t* bits, const uint8_t* pivot, con
   orc_row_den(dk, omega, den);
   memset(seg, 0, (size_t)s.bytes);
 
-  /* row factor r_i = (mean_j |S_ij| + 1e-8) / den_i, stored as binary16 */
+  /* row factor r_i = (mean_j |S_ij| + 1e-8) / den_i with mean_j |S_ij| = |M_i| mean_j |T_ij|,
+     stored as binary16; the division is a product with the plan's reciprocal 1/den_i */
   for (int i = 0; i < dk; i++) {
-    for (int j = 0; j < dv; j++) absrow[j] = fabsf(S[(long)i * dv + j]);
-    float m = tree_sum(absrow, dv) * (1.0f / (float)dv);
+    for (int j = 0; j < dv; j++) absrow[j] = fabsf(T[(long)i * dv + j]);
+    float m = (tree_sum(absrow, dv) * fabsf(M[i])) * (1.0f / (float)dv);
     if (!isfinite(m)) fl |= ORC_FLAG_NONFINITE;
     qmax[i] = pivot[i] ? 0.0f : (float)((1 << (bits[i] - 1)) - 1);
     iq[i] = pivot[i] ? 0.0f : 1.0f / qmax[i];
-    if (pivot[i]) { /* FP16 pivot row: stored raw, left out of the fit */
+    if (pivot[i]) { /* FP16 pivot row: the state value M_i T_ij stored raw, left out of the fit */
       uint8_t* row = seg + s.off_piv + 2L * dv * pivot_index(pivot, i);
       for (int j = 0; j < dv; j++) {
-        uint16_t h = orc_f32_to_f16(S[(long)i * dv + j]);
+        uint16_t h = orc_f32_to_f16(M[i] * T[(long)i * dv + j]);
         if ((h & 0x7FFFu) == 0x7C00u) fl |= ORC_FLAG_PIVOT_OVF;
         wr16(row + 2L * j, h);
       }
@@ -311,7 +324,7 @@ int orc_encode_dbg(int dk, int dv, const int8_t* bits, const uint8_t* pivot, con
       W[i] = 0.0f;
       continue;
     }
-    float r = (m + 1e-8f) / den[i];
+    float r = (m + 1e-8f) * (1.0f / den[i]);
     uint16_t rh = orc_f32_to_f16(r);
     if ((rh & 0x7FFFu) == 0x7C00u) fl |= ORC_FLAG_SCALE_OVF;
     wr16(seg + s.off_r + 2L * i, rh);
@@ -325,13 +338,15 @@ int orc_encode_dbg(int dk, int dv, const int8_t* bits, const uint8_t* pivot, con
     goto done;
   }
 
-  /* y = S / r (as a multiply by the rounded reciprocal); c0_j = max_i |y_ij| / qmax_i */
+  /* y = S / r_hat = T_ij * (M_i * (1/r_hat_i)); c0_j = max_i |y_ij| / qmax_i */
+  for (int i = 0; i < dk; i++) {
+    float rho = M[i] * ir[i];
+    for (int j = 0; j < dv; j++) y[(long)i * dv + j] = T[(long)i * dv + j] * rho;
+  }
   for (int j = 0; j < dv; j++) {
     float mx = 0.0f;
     for (int i = 0; i < dk; i++) {
-      long e = (long)i * dv + j;
-      y[e] = S[e] * ir[i];
-      float t = fabsf(y[e]) * iq[i];
+      float t = fabsf(y[(long)i * dv + j]) * iq[i];
       if (t > mx) mx = t;
     }
     c0[j] = mx;
@@ -380,6 +395,18 @@ done:
   return 0;
 }
 
+/* Encode the fp32 state S (dk x dv row-major) into seg: the requantization of S = 1 * S.
+   pre, z0_out, c0_out as for requant(). */
+int orc_encode_dbg(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const float* omega,
+                   const float* S, uint8_t* seg, double* pre, int8_t* z0_out, float* c0_out,
+                   uint32_t* flags) {
+  float* one = (float*)malloc(sizeof(float) * dk);
+  for (int i = 0; i < dk; i++) one[i] = 1.0f;
+  int rc = requant(dk, dv, bits, pivot, omega, S, one, seg, pre, z0_out, c0_out, flags);
+  free(one);
+  return rc;
+}
+
 int orc_encode(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const float* omega,
                const float* S, uint8_t* seg, double* pre, uint32_t* flags) {
   return orc_encode_dbg(dk, dv, bits, pivot, omega, S, seg, pre, NULL, NULL, flags);
@@ -389,14 +416,6 @@ int orc_encode(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const f
 /* the decode step (Method 4)                                                                 */
 /* ------------------------------------------------------------------------------------------ */
 
-/* One gated delta step, in place, on a tile given as per-row factors f_i (the binary16 row
-   factor r_hat_i of a quantized row, 1 for a pivot row or an unquantized state) times a matrix X
-   (c_j z_ij, exact; or the pivot / fp32 values), so that the decoded state is f_i X_ij:
-     u = S^T k;   S_ij <- a_i S_ij + (beta k_i) (v_j - a_i u_j);   out = S^T q
-   which is S <- A S + beta k v^T with A = Diag(a)(I - beta k k^T) (GDN: every a_i = alpha).
-   The row factor enters through the row coefficients k_i f_i and a_i f_i:
-     u_j = dot_i(k_i f_i, X_ij);  e = fma(-a_i, u_j, v_j);  S_ij = fma(a_i f_i, X_ij, (beta k_i) e)
-   With a = 1 and beta = 0 this returns S_ij = f_i X_ij rounded once: the decoded state. */
 /* Gate orders of A_t (both readings of the digest's "A_t contains the retention gate and the
    Delta update"):
      ORC_DELTA_FIRST  A = Diag(a)(I - beta k k^T): the delta update, then the decay of each row
@@ -407,26 +426,51 @@ int orc_encode(int dk, int dv, const int8_t* bits, const uint8_t* pivot, const f
    For a scalar gate (GDN) the two are the same map; their binary32 results differ in rounding. */
 #define ORC_DELTA_FIRST 0
 #define ORC_DECAY_FIRST 1
+#define ORC_GATE_ERASE 0x1p-72f   /* a gate below this erases the row's previous state */
 
-static void delta_update_readout(int dk, int dv, float* S, const float* f, const float* q,
-                                 const float* k, const float* v, const float* a, float beta,
-                                 float* out, int order) {
+/* One gated delta step on a tile given as per-row factors f_i (r_hat_i of a quantized row, 1 for a
+   pivot row or an unquantized state) times X (c_j z_ij, exact; or the pivot / fp32 values), so
+   that the stored state is f_i X_ij:
+     u_j = dot_i(kc_i, X_ij)     kc_i = k_i f_i, or k_i (a_i f_i) when the rows decay first
+     e_ij = fma(-a_i, u_j, v_j), or v_j - u_j when the rows decay first
+     T_ij = fma(K_i, e_ij, X_ij),  and the updated state is S_ij = M_i T_ij with
+     M_i = a_i f_i, K_i = (beta k_i) / M_i  (so M_i T_ij = a_i f_i X_ij + beta k_i e_ij)
+   which is S <- A S + beta k v^T with A = Diag(a)(I - beta k k^T) (GDN: every a_i = alpha), or
+   A = (I - beta k k^T) Diag(a).  A row with |a_i| < 2^-72 has its X row zeroed after u (its
+   previous state is erased: S = beta k_i e); such a row and a dead one (f_i = 0) take M_i =
+   beta k_i, K_i = 1.  out_j = dot_i(q_i M_i, T_ij).  T is updated in place (it holds X on
+   entry). */
+static void update_factored(int dk, int dv, float* T, float* M, const float* f, const float* q,
+                            const float* k, const float* v, const float* a, float beta,
+                            float* out, int order) {
   float* u = (float*)malloc(sizeof(float) * dv);
-  float* kf = (float*)malloc(sizeof(float) * dk);
-  /* row coefficient of the key projection: k_i f_i, or k_i (a_i f_i) once the rows decayed */
-  for (int i = 0; i < dk; i++) kf[i] = order == ORC_DECAY_FIRST ? k[i] * (a[i] * f[i]) : k[i] * f[i];
-  for (int j = 0; j < dv; j++) u[j] = dot_fixed(kf, 1, S + j, dv, dk);
+  float* kc = (float*)malloc(sizeof(float) * dk);
+  float* K = (float*)malloc(sizeof(float) * dk);
+  float* qm = (float*)malloc(sizeof(float) * dk);
   for (int i = 0; i < dk; i++) {
-    float bk = beta * k[i], af = a[i] * f[i];
+    float m = a[i] * f[i], bk = beta * k[i];
+    kc[i] = order == ORC_DECAY_FIRST ? k[i] * m : k[i] * f[i];
+    int erased = fabsf(a[i]) < ORC_GATE_ERASE;
+    if (erased || f[i] == 0.0f) {
+      M[i] = bk;
+      K[i] = 1.0f;
+    } else {
+      M[i] = m;
+      K[i] = bk / m;
+    }
+    qm[i] = q[i] * M[i];
+  }
+  for (int j = 0; j < dv; j++) u[j] = dot_fixed(kc, 1, T + j, dv, dk);
+  for (int i = 0; i < dk; i++) {
+    int erased = fabsf(a[i]) < ORC_GATE_ERASE;
     for (int j = 0; j < dv; j++) {
       long e = (long)i * dv + j;
       float ev = order == ORC_DECAY_FIRST ? v[j] - u[j] : fmaf(-a[i], u[j], v[j]);
-      S[e] = fmaf(af, S[e], bk * ev);
+      T[e] = fmaf(K[i], ev, erased ? 0.0f : T[e]);
     }
   }
-  for (int j = 0; j < dv; j++) out[j] = dot_fixed(q, 1, S + j, dv, dk);
-  free(u);
-  free(kf);
+  for (int j = 0; j < dv; j++) out[j] = dot_fixed(qm, 1, T + j, dv, dk);
+  free(u); free(kc); free(K); free(qm);
 }
 
 /* Splits a segment into per-row factors f (r_hat, or 1 on pivot rows) and X = c_j z_ij (exact)
@@ -450,20 +494,24 @@ static int decode_factored(int dk, int dv, const int8_t* bits, const uint8_t* pi
 }
 
 /* Decode step of one (request, head) tile, in place on seg.  a has dk entries (all equal for
-   GDN).  S_upd (optional) receives the updated fp32 state before requantization, pre (optional)
-   the final pre-rounding values.  Returns 0, or -1 on a corrupt code. */
+   GDN).  S_upd (optional) receives the updated state M_i T_ij rounded to binary32, pre
+   (optional) the final pre-rounding values.  Returns 0, or -1 on a corrupt code. */
 int orc_tile_step_dbg(int dk, int dv, const int8_t* bits, const uint8_t* pivot,
                       const float* omega, uint8_t* seg, const float* q, const float* k,
                       const float* v, const float* a, float beta, float* out, float* S_upd,
                       double* pre, int8_t* z0_out, float* c0_out, uint32_t* flags, int order) {
-  float* S = (float*)malloc(sizeof(float) * dk * dv);
-  float* f = (float*)malloc(sizeof(float) * dk);
-  int rc = decode_factored(dk, dv, bits, pivot, seg, S, f);
-  delta_update_readout(dk, dv, S, f, q, k, v, a, beta, out, order);
+  float* T = (float*)calloc((size_t)dk * dv, sizeof(float));
+  float* f = (float*)calloc((size_t)dk, sizeof(float));
+  float* M = (float*)calloc((size_t)dk, sizeof(float));
+  int rc = decode_factored(dk, dv, bits, pivot, seg, T, f);
+  update_factored(dk, dv, T, M, f, q, k, v, a, beta, out, order);
+  if (S_upd)
+    for (int i = 0; i < dk; i++)
+      for (int j = 0; j < dv; j++) S_upd[(long)i * dv + j] = M[i] * T[(long)i * dv + j];
+  requant(dk, dv, bits, pivot, omega, T, M, seg, pre, z0_out, c0_out, flags);
+  free(T);
   free(f);
-  if (S_upd) memcpy(S_upd, S, sizeof(float) * dk * dv);
-  orc_encode_dbg(dk, dv, bits, pivot, omega, S, seg, pre, z0_out, c0_out, flags);
-  free(S);
+  free(M);
   return rc;
 }
 
@@ -482,13 +530,18 @@ int orc_tile_step(int dk, int dv, const int8_t* bits, const uint8_t* pivot, cons
                          flags, ORC_DELTA_FIRST);
 }
 
-/* FP32-state mode: the same update and readout on an unquantized state (warm-up, drift). */
+/* FP32-state mode: the same update and readout on an unquantized state (warm-up, drift); the
+   state is stored back as M_i T_ij rounded to binary32. */
 void orc_fp32_step_o(int dk, int dv, float* S, const float* q, const float* k, const float* v,
                      const float* a, float beta, float* out, int order) {
-  float* f = (float*)malloc(sizeof(float) * dk);
+  float* f = (float*)calloc((size_t)dk, sizeof(float));
+  float* M = (float*)calloc((size_t)dk, sizeof(float));
   for (int i = 0; i < dk; i++) f[i] = 1.0f;
-  delta_update_readout(dk, dv, S, f, q, k, v, a, beta, out, order);
+  update_factored(dk, dv, S, M, f, q, k, v, a, beta, out, order);
+  for (int i = 0; i < dk; i++)
+    for (int j = 0; j < dv; j++) S[(long)i * dv + j] = M[i] * S[(long)i * dv + j];
   free(f);
+  free(M);
 }
 
 void orc_fp32_step(int dk, int dv, float* S, const float* q, const float* k, const float* v,

@@ -190,7 +190,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   // per-head layout (segment: code block, pivot rows, row factors, column factors)
   std::vector<int> head_type(H), off_piv(H), off_r(H), off_c(H), words(H);
   std::vector<long long> head_off(H), head_bytes(H);
-  std::vector<float> den(nrow), iq(nrow), omega(d->omega, d->omega + nrow);
+  std::vector<float> den(nrow), iq(nrow), omega(d->omega, d->omega + nrow);  // den: 1/den_i
   std::vector<int> bits(nrow), rowpos(nrow), pividx(nrow), rowmeta(nrow);
   long long off = 0;
   for (int h = 0; h < H; h++) {
@@ -239,7 +239,9 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
     // den_i = 1 + omega_i / mean(omega): mean as a pairwise tree times 1/d
     const float* ho = d->omega + (long long)h * D;
     const float mean = tree_sum(ho, D) * (1.0f / (float)D);
-    for (int i = 0; i < D; i++) den[(long long)h * D + i] = mean > 0.0f ? 1.0f + ho[i] / mean : 1.0f;
+    // the kernels scale by the reciprocal 1/den_i, rounded once here
+    for (int i = 0; i < D; i++)
+      den[(long long)h * D + i] = 1.0f / (mean > 0.0f ? 1.0f + ho[i] / mean : 1.0f);
   }
 
   // Dispatch order of the heads: the tiles with the most vector work first, the cheapest last
@@ -322,7 +324,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   dp.off_r = (const int*)at(i_or);
   dp.off_c = (const int*)at(i_oc);
   dp.words = (const int*)at(i_w);
-  dp.den = (const float*)at(i_den);
+  dp.iden = (const float*)at(i_den);
   dp.omega = (const float*)at(i_om);
   dp.iq = (const float*)at(i_iq);
   dp.bits = (const int*)at(i_bits);

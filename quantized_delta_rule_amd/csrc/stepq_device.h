@@ -20,11 +20,15 @@
 //   wave-uniform addresses (broadcast reads, no VALU work).
 //
 // Arithmetic matches a fixed binary32 evaluation order bit for bit:
-//   dequant  X_ij = c_j z_ij (exact); the row factor r_i enters through the row coefficients
-//            k_i r_i and a_i r_i (pivot rows: X = the binary16 values, factor 1)
-//   update   u = dot_i(k_i r_i, X);  e = fma(-a_i, u_j, v_j);  S = fma(a_i r_i, X, (beta k_i) e)
-//   sums     aligned groups of 4 rows accumulated with fma first to last, the group sums then
-//            added as a pairwise tree; the row magnitude sum is a pairwise tree over columns
+//   dequant  X_ij = c_j z_ij (exact); f_i = r_i (pivot rows: X = the binary16 values, f = 1)
+//   update   u = dot_i(kc_i, X) with kc_i = k_i f_i (or k_i M_i when the rows decay first);
+//            e = fma(-a_i, u_j, v_j) (or v_j - u_j);  T = fma(K_i, e, X);  the updated state is
+//            S_ij = M_i T_ij with M_i = a_i f_i, K_i = (beta k_i) / M_i (rows whose gate is
+//            below 2^-72 drop X, and they and dead rows take M_i = beta k_i, K_i = 1)
+//   scales   readout coefficient q_i M_i, row magnitude |M_i| tree_j |T_ij|, y = T (M_i / r_i)
+//   sums     one fma chain over each wave's 32 rows (first term a rounded product), the waves'
+//            partials added as a pairwise tree; the row magnitude sum is a pairwise tree over
+//            columns
 //   codes    round-half-even of the exact product y * (1/c): fma(y, 1/c, 1.5*2^23) rounds the
 //            exact product once onto the integer grid of [2^23, 2^24); the low b bits of that
 //            float are the two's-complement code, and the clamp to +-qmax is applied in the same
@@ -42,6 +46,7 @@ namespace stepq {
 namespace dev {
 
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr float kGateErase = 0x1p-72f; // a gate below this erases the row's previous state
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr unsigned kFlagNonfinite = 1u, kFlagScaleOvf = 2u, kFlagPivotOvf = 4u,
                    kFlagBadSlot = 8u;
@@ -123,15 +128,20 @@ struct Geo {
 // Per-row record, read at wave-uniform addresses (broadcast reads).  One interleaved record per
 // row keeps every field of a wave's 32 rows within ds_read's immediate offset range of a single
 // base register.  GDN rows share one gate (alpha) and one width, so they carry no a or 1/qmax.
+//   kr   key-projection coefficient k f (or k M when the rows decay first)
+//   K    (beta k) / M: the update T = fma(K, e, X)
+//   M    row scale of the updated state S = M T
+//   rho  M / r_hat (after the row factor; 0 on pivot and dead rows): y = T rho
+//   W    omega r_hat^2
 template <bool KDA>
 struct Row;
 template <>
 struct Row<false> {
-  float kr, ar, bk, q, ir, W;  // k r_hat, alpha r_hat, beta k, q, 1/r_hat, omega r_hat^2
+  float kr, K, qm, M, rho, W;  // qm: readout coefficient q M
 };
 template <>
 struct Row<true> {
-  float kr, ar, a, bk, ir, W;  // as above without q (kept in the staging area), plus the gate a
+  float kr, K, a, M, rho, W;   // the gate a; q M is kept in the staging area
   int meta;                    // packed width, stream position or pivot index (row_meta)
 };
 
@@ -265,24 +275,39 @@ __device__ __forceinline__ void raise_flags(const Args& A, unsigned fl) {
 // phases shared by the tile variants (S: this lane's 32 rows x G columns)
 // ---------------------------------------------------------------------------------------------
 
-// dot over the wave's 32 rows of a per-row scalar x_r with S[r][g]: fma chains of four, then a
-// pairwise tree over the 8 chains.
+// Per-row loop over the wave's 32 rows in groups of NG rows, software-pipelined: the
+// group's per-row coefficients (LDS broadcast reads, xr(r)) are fetched one group ahead, and a
+// scheduling fence closes each group.  Left to itself the compiler fetches all 32 coefficients
+// up front (32 registers, which spills the tile); with a fence but no look-ahead every group
+// waits for its LDS reads.  body(r, x) does the row's work with its coefficient x.
+template <int NG = 4, typename XF, typename Body>
+__device__ __forceinline__ void rows_pipelined(XF&& xr, Body&& body) {
+  constexpr int NGR = 32 / NG;  // groups
+  float x[2][NG];
+  sfor<NG>([&](auto tt) { x[0][CI(tt)] = xr(CI(tt)); });
+  sfor<NGR>([&](auto jj) {
+    constexpr int j = CI(jj);
+    if constexpr (j + 1 < NGR)
+      sfor<NG>([&](auto tt) { x[(j + 1) & 1][CI(tt)] = xr(NG * (j + 1) + CI(tt)); });
+    sfor<NG>([&](auto tt) {
+      body(std::integral_constant<int, NG * j + CI(tt)>{}, x[j & 1][CI(tt)]);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// dot over the wave's 32 rows of a per-row scalar x_r with S[r][g]: one fma chain per column,
+// first row to last.
 template <int G, typename XF>
 __device__ __forceinline__ void row_dot(const float (&S)[32][G], XF&& xr, float* res) {
-  float lv[G][4];
-  sfor<8>([&](auto mm) {
-    constexpr int m = CI(mm);
-    const float x0 = xr(4 * m), x1 = xr(4 * m + 1), x2 = xr(4 * m + 2), x3 = xr(4 * m + 3);
+  rows_pipelined(xr, [&](auto rr, float x) {
+    constexpr int r = CI(rr);
     sfor<G>([&](auto gg) {
       constexpr int g = CI(gg);
-      float s = x0 * S[4 * m][g];
-      s = __builtin_fmaf(x1, S[4 * m + 1][g], s);
-      s = __builtin_fmaf(x2, S[4 * m + 2][g], s);
-      s = __builtin_fmaf(x3, S[4 * m + 3][g], s);
-      tree_push<m>(lv[g], s);
+      if constexpr (r == 0) res[g] = x * S[0][g];
+      else res[g] = __builtin_fmaf(x, S[r][g], res[g]);
     });
   });
-  sfor<G>([&](auto gg) { res[CI(gg)] = lv[CI(gg)][3]; });
 }
 
 // Per-column error of the delta update with one gate for all rows: e = v - alpha u (the delta
@@ -359,84 +384,74 @@ __device__ __forceinline__ void put_rowabs(SM& sm, const float (&S)[32][Geo<D>::
   });
 }
 
-// Row factor of row 32w + (lane & 31): lanes L and L+32 each sum half of the row's columns, the
-// halves are added, and lane L < 32 writes r_hat to the pool (unless rblk is null) and
-// ir = 1/r_hat (0 if dead or pivot) and W = (omega r_hat) r_hat (0 likewise) into the row
-// record.
+// Row factor of row 32w + (lane & 31): lanes L and L+32 each sum half of the row's |T| over its
+// columns, the halves are added and scaled by |M|, and lane L < 32 writes r_hat to the pool
+// (unless rblk is null) and rho = M (1/r_hat) (0 if dead or pivot) and W = (omega r_hat) r_hat
+// (0 likewise) into the row record, whose rho and W slots hold the plan's 1/den and omega of
+// the row until then.
 template <int D, typename SM>
-__device__ __forceinline__ void row_factor(SM& sm, int lane, int row, float den, float om,
-                                           bool piv, uint16_t* rblk, unsigned& fl) {
+__device__ __forceinline__ void row_factor(SM& sm, int lane, int row, bool piv, uint16_t* rblk,
+                                           unsigned& fl) {
   float lv[6];
   const float* const src = lds_pin(
       sm, sm.tr + (threadIdx.x >> 6) * SM::kSec + (lane & 31) * 65 + (lane & 32));
   sfor<32>([&](auto jj) { tree_push<CI(jj)>(lv, src[CI(jj)]); });
   const float other = __shfl_xor(lv[5], 32);
-  const float m = (lane < 32 ? lv[5] + other : other + lv[5]) * (1.0f / (float)D);
+  const float Mr = sm.row[row].M;
+  const float m =
+      ((lane < 32 ? lv[5] + other : other + lv[5]) * __builtin_fabsf(Mr)) * (1.0f / (float)D);
   if (!__builtin_isfinite(m)) fl |= kFlagNonfinite;
   if (lane >= 32) return;
   if (piv) {
-    sm.row[row].ir = 0.0f;
+    sm.row[row].rho = 0.0f;
     sm.row[row].W = 0.0f;
     if (rblk) rblk[row] = 0;
     return;
   }
-  const float r = (m + 1e-8f) / den;
+  const float iden = sm.row[row].rho, om = sm.row[row].W;  // parked there by load_inputs
+  const float r = (m + 1e-8f) * iden;
   const uint16_t rh = f2h(r);
   if (is_inf16(rh)) fl |= kFlagScaleOvf;
   if (rblk) rblk[row] = rh;
   const float rf = h2f(rh);
-  sm.row[row].ir = rcp16(rf);
+  sm.row[row].rho = Mr * rcp16(rf);
   sm.row[row].W = (om * rf) * rf;
 }
 
-// y = S * ir (in place) and the column maximum max_i |y| of a one-width (GDN) tile: the 1/qmax
+// y = T * rho (in place) and the column maximum max_i |y| of a one-width (GDN) tile: the 1/qmax
 // factor is applied after the maximum (rounding is monotone).
 template <int G, typename RW>
 __device__ __forceinline__ void scale_rows(float (&S)[32][G], const RW& rows, float* mx) {
   sfor<G>([&](auto gg) { mx[CI(gg)] = 0.0f; });
-  sfor<32>([&](auto rr) {
+  rows_pipelined([&](int r) { return rows.r[r].rho; }, [&](auto rr, float rho) {
     constexpr int r = CI(rr);
-    const float ir = rows.r[r].ir;
     sfor<G>([&](auto gg) {
       constexpr int g = CI(gg);
-      S[r][g] = S[r][g] * ir;
+      S[r][g] = S[r][g] * rho;
       mx[g] = __builtin_fmaxf(mx[g], __builtin_fabsf(S[r][g]));
     });
   });
 }
 
 // First quantization z0 = rne(y / c0) and the sums of the omega-weighted least-squares fit:
-// num = sum_i (W_i z0) y, sq = sum_i (W_i z0) z0, both as fma chains of four + pairwise tree.
+// num = sum_i (W_i z0) y, sq = sum_i (W_i z0) z0, each one fma chain over the wave's rows.
 template <int G, typename RW>
 __device__ __forceinline__ void ls_sums(const float (&S)[32][G], const RW& rows, const float* ic0,
                                         float* num, float* sq) {
-  float ln[G][4], ls[G][4];
-  sfor<8>([&](auto mm) {
-    constexpr int m = CI(mm);
-    float W4[4];
-    sfor<4>([&](auto tt) { W4[CI(tt)] = rows.r[4 * m + CI(tt)].W; });
+  rows_pipelined([&](int r) { return rows.r[r].W; }, [&](auto rr, float W) {
+    constexpr int r = CI(rr);
     sfor<G>([&](auto gg) {
       constexpr int g = CI(gg);
-      float sn = 0.0f, sqv = 0.0f;
-      sfor<4>([&](auto tt) {
-        constexpr int r = 4 * m + CI(tt);
-        const float z0 = __builtin_fmaf(S[r][g], ic0[g], kMagic) - kMagic;  // |z0| <= qmax
-        const float a = W4[CI(tt)] * z0;
-        if constexpr (CI(tt) == 0) {
-          sn = a * S[r][g];
-          sqv = a * z0;
-        } else {
-          sn = __builtin_fmaf(a, S[r][g], sn);
-          sqv = __builtin_fmaf(a, z0, sqv);
-        }
-      });
-      tree_push<m>(ln[g], sn);
-      tree_push<m>(ls[g], sqv);
+      const float z0 = __builtin_fmaf(S[r][g], ic0[g], kMagic) - kMagic;  // |z0| <= qmax
+      const float a = W * z0;
+      if constexpr (r == 0) {
+        num[g] = a * S[r][g];
+        sq[g] = a * z0;
+      } else {
+        num[g] = __builtin_fmaf(a, S[r][g], num[g]);
+        sq[g] = __builtin_fmaf(a, z0, sq[g]);
+      }
     });
-  });
-  sfor<G>([&](auto gg) {
-    num[CI(gg)] = ln[CI(gg)][3];
-    sq[CI(gg)] = ls[CI(gg)][3];
   });
 }
 
@@ -463,18 +478,25 @@ __device__ __forceinline__ void store_out(const StepArgs& A, long long tile, int
 }
 
 // Split-mode hand-over of the update factors: a_i, beta k_i per row (lane L < 32 of each
-// wave); per column (wave 0) either e_j (UV false: GDN, or any gate decaying the rows first) or
-// u_j and v_j (UV true: per-row gate applied after the delta update, e_ij = v_j - a_i u_j).
-template <int D, bool UV>
-__device__ __forceinline__ void put_stash(const StepArgs& A, long long tile, int w, int lane,
-                                          int row, float a_row, float bk_row, const float* e,
-                                          const float* u, const float* vv) {
-  constexpr int G = Geo<D>::G;
+// wave, written as soon as they are loaded); per column (wave 0, after the readout) either e_j
+// (UV false: GDN, or any gate decaying the rows first) or u_j and v_j (UV true: per-row gate
+// applied after the delta update, e_ij = v_j - a_i u_j).
+template <int D>
+__device__ __forceinline__ void put_stash_rows(const StepArgs& A, long long tile, int lane,
+                                               int row, float a_row, float bk_row) {
   float* st = A.stash + tile * 4 * D;
   if (lane < 32) {
     st[row] = a_row;
     st[D + row] = bk_row;
   }
+}
+
+template <int D, bool UV>
+__device__ __forceinline__ void put_stash_cols(const StepArgs& A, long long tile, int w,
+                                               int lane, const float* e, const float* u,
+                                               const float* vv) {
+  constexpr int G = Geo<D>::G;
+  float* st = A.stash + tile * 4 * D;
   if (w == 0) {
     sfor<G>([&](auto gg) {
       constexpr int g = CI(gg);
@@ -499,13 +521,19 @@ __device__ __forceinline__ void load_state(const StepArgs& A, long long tile, in
 }
 
 // Per-tile inputs of a step: row records (lanes 0..31 of each wave fill their wave's rows),
-// per-column v or the hand-over.  Returns alpha (GDN) and fills vv / e / u.  UV: the hand-over
-// carries u and v (per-row e) instead of e.  The key-projection coefficient of a row is k_i r_i,
-// or k_i (a_i r_i) when the gate decays the rows before the delta update (plan order 1).
+// per-column v or the hand-over.  Returns alpha (GDN) and fills vv / e / u, and each lane's row
+// gate a_row and beta k (bk_row) for the split-mode hand-over.  UV: the hand-over carries u and v
+// (per-row e) instead of e.  The row records get M = a f (f = r_hat, or 1 on pivot rows and
+// FP16 pivot heads), K = (beta k) / M -- or M = beta k, K = 1 for a row whose gate is below
+// 2^-72 (its state is erased) or whose factor is 0 -- the key-projection coefficient k f, or
+// k M when the gate decays the rows before the delta update (plan order 1), and the readout
+// coefficient q M.  Encoding: M = 1.
 template <int D, int MODE, bool KDA, bool UV = KDA, typename SM>
 __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long tile, int h,
                                             int lane, int row, const uint16_t* rblk,
-                                            float& alpha, float* vv, float* e, float* u) {
+                                            float& alpha, float* vv, float* e, float* u,
+                                            float& a_row, float& bk_row) {
+  constexpr bool kWrite = MODE != READ;
   constexpr int G = Geo<D>::G;
   constexpr bool kRead = MODE == FUSED || MODE == READ;
   if constexpr (kRead) {
@@ -526,12 +554,18 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
   }
   // Every load first, in all lanes (lanes 32..63 read the same rows as lanes 0..31), then the
   // arithmetic and the record writes of lanes 0..31: the tile waits for memory once.  Without
-  // stored row factors (FP16 pivot heads, encoding) a 16-bit word of the head's den row is read
-  // in their place and not used.
-  const uint16_t* const rsrc = rblk ? rblk : reinterpret_cast<const uint16_t*>(A.P.den + h * D);
+  // stored row factors (FP16 pivot heads, encoding) a 16-bit word of the head's 1/den row is
+  // read in their place and not used.
+  const uint16_t* const rsrc = rblk ? rblk : reinterpret_cast<const uint16_t*>(A.P.iden + h * D);
   const uint16_t rh = rsrc[row];
   int meta = 0;
   if constexpr (KDA) meta = A.P.rowmeta[h * D + row];
+  // the row factor's plan values ride in the record's rho and W slots until row_factor()
+  float iden = 1.0f, om = 0.0f;
+  if constexpr (kWrite) {
+    iden = A.P.iden[h * D + row];
+    om = A.P.omega[h * D + row];
+  }
   float a = alpha, beta = 0.0f, kk = 0.0f, qv = 0.0f, bk = 0.0f;
   if constexpr (kRead) {
     beta = A.beta[tile];
@@ -544,21 +578,50 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
     a = st[row];
     bk = st[D + row];
   }
+  if constexpr (kRead) bk = beta * kk;
+  a_row = a;
+  bk_row = bk;
   if (lane < 32) {
     auto& rec = sm.row[row];
     // row factor: r_hat of a quantized row; 1 on pivot rows and FP16 pivot heads
     const float rf = rblk && !(KDA && meta_pivot(meta)) ? h2f(rh) : 1.0f;
-    if constexpr (KDA) rec.meta = meta;
-    if constexpr (kRead) {
-      const float ar = a * rf;
-      rec.kr = A.P.order ? kk * ar : kk * rf;
-      rec.bk = beta * kk;
-      if constexpr (KDA) sm.tr[SM::kKdaQ + row] = qv;
-      else rec.q = qv;
+    if constexpr (KDA) {
+      rec.meta = meta;
+      rec.a = a;
     }
-    if constexpr (MODE == WRITE) rec.bk = bk;
-    if constexpr (KDA) rec.a = a;
-    rec.ar = a * rf;
+    rec.rho = iden;
+    rec.W = om;
+    if constexpr (MODE == ENCODE) {
+      rec.M = 1.0f;
+    } else {
+      const float m = a * rf;
+      const bool flat = __builtin_fabsf(a) < kGateErase || rf == 0.0f;
+      const float Mv = flat ? bk : m;
+      rec.M = Mv;
+      rec.K = flat ? 1.0f : bk / m;
+      if constexpr (kRead) {
+        rec.kr = A.P.order ? kk * m : kk * rf;
+        if constexpr (KDA) sm.tr[SM::kKdaQ + row] = qv * Mv;
+        else rec.qm = qv * Mv;
+      }
+    }
+  }
+}
+
+// A gate below 2^-72 erases its row's previous state: the decoded row is dropped after the key
+// projection has used it (rows in the bits of `mask`, wave-uniform).  The zeros are written by
+// volatile moves so that they stay inside the rarely taken branch (as plain stores of 0 the
+// compiler materializes them on the common path).
+template <int G>
+__device__ __forceinline__ void erase_rows(float (&S)[32][G], uint64_t mask) {
+  if (mask) {
+#pragma unroll
+    for (int r = 0; r < 32; r++) {
+      if ((mask >> r) & 1) {
+#pragma unroll
+        for (int g = 0; g < G; g++) asm volatile("v_mov_b32 %0, 0" : "=v"(S[r][g]));
+      }
+    }
   }
 }
 
@@ -597,13 +660,10 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
     });
     sfor<G>([&](auto gg) { cc[CI(gg)] = h2f(cblk[G * lane + CI(gg)]); });
   }
-  float den = 1.0f, om = 0.0f;
-  if constexpr (kWrite) {
-    den = A.P.den[h * D + row];
-    om = A.P.omega[h * D + row];
-  }
+  float a_row, bk_row;
   load_inputs<D, MODE, false>(A, sm, tile, h, lane, row, MODE != ENCODE ? rblk : nullptr, alpha,
-                              vv, e, u);
+                              vv, e, u, a_row, bk_row);
+  if constexpr (MODE == READ) put_stash_rows<D>(A, tile, lane, row, a_row, bk_row);
   wave_lds_sync();
 
   if constexpr (MODE == ENCODE) {
@@ -624,24 +684,21 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
       xwave_sum<D>(sm, 0, lane, u);
       col_error<G>(A.P.order, alpha, u, vv, e);
     }
+    erase_rows<G>(S, __builtin_fabsf(alpha) < kGateErase ? ~0ull : 0ull);
 
-    // ---- phase 2: gated delta update and readout
-    sfor<R>([&](auto rr) {
-      constexpr int r = CI(rr);
-      const float ar = rows.r[r].ar, bk = rows.r[r].bk;
-      sfor<G>([&](auto gg) {
-        S[r][CI(gg)] = __builtin_fmaf(ar, S[r][CI(gg)], bk * e[CI(gg)]);
-      });
+    // ---- phase 2: gated delta update T = fma(K, e, X) (the state is M T) and readout
+    rows_pipelined([&](int r) { return rows.r[r].K; }, [&](auto rr, float K) {
+      sfor<G>([&](auto gg) { S[CI(rr)][CI(gg)] = __builtin_fmaf(K, e[CI(gg)], S[CI(rr)][CI(gg)]); });
     });
     if constexpr (kRead) {
       float o[G];
-      row_dot<G>(S, [&](int r) { return rows.r[r].q; }, o);
+      row_dot<G>(S, [&](int r) { return rows.r[r].qm; }, o);
       xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
       xwave_sum<D>(sm, 1, lane, o);
       store_out<D>(A, tile, w, lane, o);
       if constexpr (MODE == READ) {
-        put_stash<D, false>(A, tile, w, lane, row, alpha, sm.row[row].bk, e, u, vv);
+        put_stash_cols<D, false>(A, tile, w, lane, e, u, vv);
         return;
       }
     }
@@ -650,10 +707,10 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
     // ---- row factor from the row magnitudes
     put_rowabs<D>(sm, S, lane);
     wave_lds_sync();
-    row_factor<D>(sm, lane, row, den, om, false, rblk, fl);
+    row_factor<D>(sm, lane, row, false, rblk, fl);
     wave_lds_sync();
 
-    // ---- phase 3: y = S / r_hat, first column factor c0 = max_i |y_ij| / qmax
+    // ---- phase 3: y = S / r_hat = T M / r_hat, first column factor c0 = max_i |y_ij| / qmax
     float mx[G];
     scale_rows<G>(S, rows, mx);
     xwave_max_put<D>(sm, w, lane, mx);
@@ -717,7 +774,9 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, long long s
       });
     });
   }
-  load_inputs<D, MODE, false>(A, sm, tile, h, lane, row, nullptr, alpha, vv, e, u);
+  float a_row, bk_row;
+  load_inputs<D, MODE, false>(A, sm, tile, h, lane, row, nullptr, alpha, vv, e, u, a_row, bk_row);
+  if constexpr (MODE == READ) put_stash_rows<D>(A, tile, lane, row, a_row, bk_row);
   wave_lds_sync();
   if constexpr (MODE != ENCODE) {
     if constexpr (kRead) {
@@ -727,22 +786,21 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, long long s
       xwave_sum<D>(sm, 0, lane, u);
       col_error<G>(A.P.order, alpha, u, vv, e);
     }
+    erase_rows<G>(S, __builtin_fabsf(alpha) < kGateErase ? ~0ull : 0ull);
     sfor<R>([&](auto rr) {
       constexpr int r = CI(rr);
-      const float ar = rows.r[r].ar, bk = rows.r[r].bk;
-      sfor<G>([&](auto gg) {
-        S[r][CI(gg)] = __builtin_fmaf(ar, S[r][CI(gg)], bk * e[CI(gg)]);
-      });
+      const float K = rows.r[r].K;
+      sfor<G>([&](auto gg) { S[r][CI(gg)] = __builtin_fmaf(K, e[CI(gg)], S[r][CI(gg)]); });
     });
     if constexpr (kRead) {
       float o[G];
-      row_dot<G>(S, [&](int r) { return rows.r[r].q; }, o);
+      row_dot<G>(S, [&](int r) { return rows.r[r].qm; }, o);
       xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
       xwave_sum<D>(sm, 1, lane, o);
       store_out<D>(A, tile, w, lane, o);
       if constexpr (MODE == READ) {
-        put_stash<D, false>(A, tile, w, lane, row, alpha, sm.row[row].bk, e, u, vv);
+        put_stash_cols<D, false>(A, tile, w, lane, e, u, vv);
         return;
       }
     }
@@ -750,14 +808,15 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, long long s
   if constexpr (kWrite) {
     put_rowabs<D>(sm, S, lane);
     sfor<R>([&](auto rr) {
+      const float M = rows.r[CI(rr)].M;
       sfor<G>([&](auto gg) {
-        const uint16_t hv = f2h(S[CI(rr)][CI(gg)]);
+        const uint16_t hv = f2h(S[CI(rr)][CI(gg)] * M);
         if (is_inf16(hv)) fl |= kFlagPivotOvf;
         hblk[(row0 + CI(rr)) * D + G * lane + CI(gg)] = hv;
       });
     });
     wave_lds_sync();
-    row_factor<D>(sm, lane, row, 1.0f, 0.0f, true, nullptr, fl);
+    row_factor<D>(sm, lane, row, true, nullptr, fl);
   }
   raise_flags(A, fl);
 }
@@ -814,13 +873,10 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     const uint16_t* const cread = nwords > 0 ? cblk : pblk;
     sfor<G>([&](auto gg) { cc[CI(gg)] = h2f(cread[G * lane + CI(gg)]); });
   }
-  float den = 1.0f, om = 0.0f;
-  if constexpr (kWrite) {
-    den = A.P.den[h * D + row];
-    om = A.P.omega[h * D + row];
-  }
+  float a_row, bk_row;
   load_inputs<D, MODE, true, kUV>(A, sm, tile, h, lane, row, MODE != ENCODE ? rblk : nullptr,
-                                  alpha, vv, e, u);
+                                  alpha, vv, e, u, a_row, bk_row);
+  if constexpr (MODE == READ) put_stash_rows<D>(A, tile, lane, row, a_row, bk_row);
   if constexpr (MODE != ENCODE) {
     sfor<kStageIt>([&](auto ii) {
       const int x = tid + CI(ii) * NT;
@@ -880,15 +936,17 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     if constexpr (!kUV) sfor<G>([&](auto gg) { e[CI(gg)] = vv[CI(gg)] - u[CI(gg)]; });
   }
 
-  // ---- phase 2: update, readout
+  // ---- phase 2: update T = fma(K, e, X) (the state is M T), readout
   if constexpr (MODE != ENCODE) {
+    erase_rows<G>(S, __builtin_amdgcn_ballot_w64(lane < 32 &&
+                                                 __builtin_fabsf(a_row) < kGateErase));
     sfor<R>([&](auto rr) {
       constexpr int r = CI(rr);
-      const float a = rows.r[r].a, ar = rows.r[r].ar, bk = rows.r[r].bk;
+      const float a = rows.r[r].a, K = rows.r[r].K;
       sfor<G>([&](auto gg) {
         constexpr int g = CI(gg);
         const float ev = kUV ? __builtin_fmaf(-a, u[g], vv[g]) : e[g];
-        S[r][g] = __builtin_fmaf(ar, S[r][g], bk * ev);
+        S[r][g] = __builtin_fmaf(K, ev, S[r][g]);
       });
     });
     if constexpr (kRead) {
@@ -900,7 +958,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
       xwave_sum<D>(sm, 1, lane, o);
       store_out<D>(A, tile, w, lane, o);
       if constexpr (MODE == READ) {
-        put_stash<D, kUV>(A, tile, w, lane, row, sm.row[row].a, sm.row[row].bk, e, u, vv);
+        put_stash_cols<D, kUV>(A, tile, w, lane, e, u, vv);
         return;
       }
     }
@@ -909,7 +967,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     put_rowabs<D>(sm, S, lane);
     wave_lds_sync();
     const bool piv = meta_pivot(sm.row[row].meta);
-    row_factor<D>(sm, lane, row, den, om, piv, rblk, fl);
+    row_factor<D>(sm, lane, row, piv, rblk, fl);
     __syncthreads();  // every wave's transposes are done: zero the code staging for packing
     {
       const int n4 = nwords * 16;
@@ -936,8 +994,9 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
           constexpr int r = r0 + CI(tt);
           if (meta_pivot(ms[CI(tt)])) {
             const int pv = meta_low(ms[CI(tt)]);
+            const float M = rows.r[r].M;
             sfor<G>([&](auto gg) {
-              const uint16_t hv = f2h(S[r][CI(gg)]);
+              const uint16_t hv = f2h(S[r][CI(gg)] * M);
               if (is_inf16(hv)) fl |= kFlagPivotOvf;
               pblk[pv * D + G * lane + CI(gg)] = hv;
             });
@@ -946,10 +1005,10 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
       }
       sfor<8>([&](auto tt) {
         constexpr int r = r0 + CI(tt);
-        const float ir = rows.r[r].ir, iq = iqs[CI(tt)];
+        const float rho = rows.r[r].rho, iq = iqs[CI(tt)];
         sfor<G>([&](auto gg) {
           constexpr int g = CI(gg);
-          S[r][g] = S[r][g] * ir;
+          S[r][g] = S[r][g] * rho;
           mx[g] = __builtin_fmaxf(mx[g], __builtin_fabsf(S[r][g]) * iq);
         });
       });

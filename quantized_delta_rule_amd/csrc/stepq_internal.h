@@ -30,7 +30,7 @@ struct DevPlan {
   const int* off_r;          // [H] row-factor block offset
   const int* off_c;          // [H] column-factor block offset
   const int* words;          // [H] words per lane of the code block
-  const float* den;          // [H*d] 1 + omega_i / mean(omega)
+  const float* iden;         // [H*d] 1 / den_i, den_i = 1 + omega_i / mean(omega)
   const float* omega;        // [H*d]
   const float* iq;           // [H*d] 1/qmax, 0 on pivot rows
   const int* bits;           // [H*d] width (0 on pivot rows)

@@ -14,28 +14,33 @@ bound of the boundary between the two; the replay then continues with the binary
 
 Error bounds (unit roundoff u = 2^-24, gamma(n) = n u / (1 - n u); every bound uses the binary64
 values in place of the exact ones, whose difference is far below these bounds):
-  key projection u_j   the specification's dot is fma chains over aligned groups of 4 rows, then
-                       a pairwise tree over the d_k / 4 group sums, with the row coefficient
-                       k_i r_i rounded once: each term sees at most DOT_DEPTH roundings, so
-                       |u32 - u| <= gamma(DOT_DEPTH) sum_l |k_l S_hat_lj| (one more for the
-                       decay-first coefficient k_i (a_i r_i)).
+  key projection u_j   the specification's dot is one fma chain over each block of 32 rows (the
+                       first term a rounded product), then a pairwise tree over the d_k / 32
+                       block sums, with the row coefficient k_i r_i rounded once: each term
+                       sees at most DOT_DEPTH roundings, so |u32 - u| <= gamma(DOT_DEPTH)
+                       sum_l |k_l S_hat_lj| (one more for the decay-first coefficient
+                       k_i (a_i r_i)).
   error e              e = v - a_i u (one fma) or v - u: |e32 - e| <= u|e| + |a_i| |u32 - u|.
-  state S_ij           S = fma(a_i r_i, X, (beta k_i) e): |S32 - S| <= u|S| + (1 + u)(u|a_i S_hat|
-                       + |beta k_i| ((1 + gamma(2))|e32 - e| + gamma(2)|e|)).  Call it B_ij.
-  readout o_j          dot of q with S32: gamma(DOT_DEPTH) sum_i |q_i S_ij| + sum_i |q_i| B_ij.
-  row factor r_i       tree over d_v columns of |S32| (ROW_DEPTH levels), exact 1/d_v, + 1e-8f,
-                       / den (den's own binary32 rounding: ROW_DEPTH + 3 roundings):
-                       r rel. gamma(ROW_DEPTH + 5) + sum_j B_ij / (d_v den_i).
-  y = S32 * (1/r_hat)  |y32 - S/r_hat| <= B / r_hat + gamma(2) |S / r_hat|.
+  state S_ij           the specification keeps S = M_i T_ij with M = fl(a_i r_i),
+                       K = fl(fl(beta k_i) / M), T = fma(K, e32, X): M T = (a_i S_hat (1 + d1)
+                       + beta k_i e32 (1 + d2)(1 + d3))(1 + d5), so |S32 - S| <= gamma(2)
+                       |a_i S_hat| + |beta k_i| (gamma(4)|e| + (1 + gamma(3))|e32 - e|).  Call it
+                       B_ij (S32 being the exact product M_i T_ij).
+  readout o_j          dot of (q_i M_i rounded) with T: gamma(DOT_DEPTH) sum_i |q_i S_ij| +
+                       sum_i |q_i| B_ij.
+  row factor r_i       tree over d_v columns of |T| (ROW_DEPTH levels), times |M_i|, exact 1/d_v,
+                       + 1e-8f, times the rounded 1/den (den's own binary32 rounding: ROW_DEPTH +
+                       3 roundings): r rel. gamma(ROW_DEPTH + 8) + sum_j B_ij / (d_v den_i).
+  y = T * (M_i/r_hat)  |y32 - S/r_hat| <= B / r_hat + gamma(3) |S / r_hat|.
   c0_j                 max over rows of (|y| * (1/qmax)) rounded twice more: per candidate
-                       |.| <= (B/r_hat + gamma(4)|S/r_hat|) / qmax.
+                       |.| <= (B/r_hat + gamma(5)|S/r_hat|) / qmax.
   first codes          t0 = y * (1/c0) exact product: |t0_32 - t0| <= (B/r_hat)/c0 + |t0|
-                       (gamma(3) + 2 dc0/c0) (1 + 2 dc0/c0).
+                       (gamma(4) + 2 dc0/c0) (1 + 2 dc0/c0).
   refit sums           W = omega r_hat^2 (2 roundings), a = W z0 (1), num = dot(a, y),
                        sq = dot(a, z0) (DOT_DEPTH - 1 more); every term is >= 0 (z0 and y share
                        their sign), so num, sq carry relative errors gamma(DOT_DEPTH + 2) plus
                        sum_i W_i |z0_ij| |y32 - y| / num; c1 = num / sq adds u.
-  final codes          t = y * (1/c_hat): |t32 - t| <= (B/r_hat)/c_hat + gamma(4)|t|.
+  final codes          t = y * (1/c_hat): |t32 - t| <= (B/r_hat)/c_hat + gamma(5)|t|.
   pivot values         |S32 - S| <= B_ij.
 Every bound is multiplied by SAFETY.
 """
@@ -48,7 +53,7 @@ import numpy as np
 from oracle import codec, plain
 
 U = 2.0 ** -24
-DOT_DEPTH = 10      # 4 (chain of four) + log2(128 / 4) tree levels + 1 (rounded coefficient)
+DOT_DEPTH = 35      # 32 (one chain per block of 32 rows) + log2(128 / 32) + 1 (coefficient)
 ROW_DEPTH = 7       # pairwise tree over 128 values
 SAFETY = 1.25
 EPS_SPEC = float(np.float32(1e-8))   # the specification's 1e-8f
@@ -183,8 +188,7 @@ def check_step(bits, pivot, omega, order, seg_before, seg_after, out_side, z0_si
         eps_u = gam(DOT_DEPTH + 1) * (np.abs(a)[:, None] * kS).sum(axis=0)
         eps_e = U * np.abs(e) + eps_u[None, :]
     bk = np.abs(beta * k)[:, None]
-    B = U * np.abs(S) + (1 + U) * (U * np.abs(a[:, None] * S_hat)
-                                   + bk * ((1 + gam(2)) * eps_e + gam(2) * np.abs(e)))
+    B = gam(2) * np.abs(a[:, None] * S_hat) + bk * (gam(4) * np.abs(e) + (1 + gam(3)) * eps_e)
     B = SAFETY * B + 2.0 ** -140
 
     # ---- readout
@@ -214,8 +218,8 @@ def check_step(bits, pivot, omega, order, seg_before, seg_after, out_side, z0_si
     den = plain.row_den(om)
     r64 = plain.row_factor(S, den)
     absS = np.abs(S).sum(axis=1)
-    br = SAFETY * (r64 * gam(ROW_DEPTH + 5)
-                   + ((gam(ROW_DEPTH) * absS + (1 + gam(ROW_DEPTH)) * B.sum(axis=1)) / dv
+    br = SAFETY * (r64 * gam(ROW_DEPTH + 8)
+                   + ((gam(ROW_DEPTH + 1) * absS + (1 + gam(ROW_DEPTH + 1)) * B.sum(axis=1)) / dv
                       + abs(EPS_SPEC - plain.EPS_ROW)) / den * (1 + gam(3)))
     q_rows = ~piv
     _check_f16("r", r64[q_rows], r16_s[q_rows], br[q_rows], st, where + " row factors")
@@ -225,7 +229,7 @@ def check_step(bits, pivot, omega, order, seg_before, seg_after, out_side, z0_si
 
     # ---- first column factors and first codes
     y = S / rl[:, None]
-    by = B / rl[:, None] + gam(2) * np.abs(y)
+    by = B / rl[:, None] + gam(3) * np.abs(y)
     c0 = plain.column_init(S, r_hat, np.where(piv, 1.0, qm), live)
     cand = np.where(live[:, None], (by + gam(2) * np.abs(y)) / np.where(piv, 1.0, qm)[:, None], 0)
     bc0 = SAFETY * cand.max(axis=0)
@@ -238,7 +242,7 @@ def check_step(bits, pivot, omega, order, seg_before, seg_after, out_side, z0_si
     c0s = np.where(c0 > 0, c0, 1.0)
     rc = np.where(c0 > 0, bc0 / c0s, 0.0)
     t0 = plain.scaled(S, r_hat, c0, live)
-    bt0 = SAFETY * ((B / rl[:, None]) / c0s[None, :] + np.abs(t0) * (gam(3) + 2 * rc[None, :])) \
+    bt0 = SAFETY * ((B / rl[:, None]) / c0s[None, :] + np.abs(t0) * (gam(4) + 2 * rc[None, :])) \
         * (1 + 2 * rc[None, :])
     m0 = live[:, None] & (c0 > 0)[None, :]
     z0_side = np.asarray(z0_side, np.float64)
@@ -263,7 +267,7 @@ def check_step(bits, pivot, omega, order, seg_before, seg_after, out_side, z0_si
     # ---- final codes
     t = plain.scaled(S, r_hat, c_hat, live)
     cs = np.where(c_hat != 0, c_hat, 1.0)
-    bt = SAFETY * ((B / rl[:, None]) / cs[None, :] + gam(4) * np.abs(t))
+    bt = SAFETY * ((B / rl[:, None]) / cs[None, :] + gam(5) * np.abs(t))
     m = live[:, None] & (c_hat != 0)[None, :]
     z_s = np.asarray(z_s, np.float64)
     if np.any(z_s[~m] != 0):
@@ -294,7 +298,7 @@ def check_encode(bits, pivot, omega, S32, seg_after, z0_side, where="",
         return st
     den = plain.row_den(om)
     r64 = plain.row_factor(S, den)
-    br = SAFETY * (r64 * gam(ROW_DEPTH + 5) + (gam(ROW_DEPTH) * np.abs(S).sum(axis=1) / dv
+    br = SAFETY * (r64 * gam(ROW_DEPTH + 8) + (gam(ROW_DEPTH + 1) * np.abs(S).sum(axis=1) / dv
                                                + abs(EPS_SPEC - plain.EPS_ROW)) / den)
     _check_f16("r", r64[~piv], r16_s[~piv], br[~piv], st, where + " row factors")
     r_hat = np.where(piv, 0.0, plain.f16(r16_s))
@@ -302,12 +306,12 @@ def check_encode(bits, pivot, omega, S32, seg_after, z0_side, where="",
     rl = np.where(live, r_hat, 1.0)
     y = S / rl[:, None]
     c0 = plain.column_init(S, r_hat, np.where(piv, 1.0, qm), live)
-    cand = np.where(live[:, None], gam(4) * np.abs(y) / np.where(piv, 1.0, qm)[:, None], 0)
+    cand = np.where(live[:, None], gam(5) * np.abs(y) / np.where(piv, 1.0, qm)[:, None], 0)
     bc0 = SAFETY * cand.max(axis=0)
     c0s = np.where(c0 > 0, c0, 1.0)
     rc = np.where(c0 > 0, bc0 / c0s, 0.0)
     t0 = plain.scaled(S, r_hat, c0, live)
-    bt0 = SAFETY * np.abs(t0) * (gam(3) + 2 * rc[None, :]) * (1 + 2 * rc[None, :])
+    bt0 = SAFETY * np.abs(t0) * (gam(4) + 2 * rc[None, :]) * (1 + 2 * rc[None, :])
     m0 = live[:, None] & (c0 > 0)[None, :]
     z0_side = np.asarray(z0_side, np.float64)
     _check_codes("z0", np.where(m0, t0, 0.0), np.where(m0, z0_side, 0.0),
@@ -316,14 +320,14 @@ def check_encode(bits, pivot, omega, S32, seg_after, z0_side, where="",
     c1 = plain.refit(S, r_hat, z0, om, c0, live)
     W = np.where(live, om * r_hat * r_hat, 0.0)
     num = (W[:, None] * z0 * y).sum(axis=0)
-    dnum = (W[:, None] * np.abs(z0) * gam(2) * np.abs(y)).sum(axis=0)
+    dnum = (W[:, None] * np.abs(z0) * gam(3) * np.abs(y)).sum(axis=0)
     sq = (W[:, None] * z0 * z0).sum(axis=0)
     rel_c1 = U + 2 * gam(DOT_DEPTH + 2) + dnum / np.where(num > 0, num, 1.0)
     bc1 = SAFETY * np.where(sq > 0, np.abs(c1) * rel_c1 * (1 + gam(4)), bc0)
     _check_f16("c", c1, c16_s, bc1, st, where + " column factors")
     c_hat = plain.f16(c16_s)
     t = plain.scaled(S, r_hat, c_hat, live)
-    bt = SAFETY * gam(4) * np.abs(t)
+    bt = SAFETY * gam(5) * np.abs(t)
     m = live[:, None] & (c_hat != 0)[None, :]
     z_s = np.asarray(z_s, np.float64)
     _check_codes("z", np.where(m, t, 0.0), np.where(m, z_s, 0.0), np.where(piv, 0.0, qm),

@@ -20,25 +20,36 @@ def _fma32(a, b, c):
     return np.float32(Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c)))
 
 
+def _chain(x, y):
+    s = np.float32(x[0] * y[0])
+    for t in range(1, len(x)):
+        s = _fma32(x[t], y[t], s)
+    return s
+
+
 def test_dot_order_pin(orc):
-    # group of four: s = x0*y0; s = fma(x1,y1,s); s = fma(x2,y2,s); s = fma(x3,y3,s)
+    # blocks of 32: s = x0*y0, then s = fma(x_i, y_i, s) first to last; block sums by tree()
     g = np.random.default_rng(7)
-    for _ in range(200):
-        x = g.standard_normal(8).astype(np.float32)
-        y = g.standard_normal(8).astype(np.float32)
-        quads = []
-        for m in range(2):
-            s = np.float32(x[4 * m] * y[4 * m])
-            for t in range(1, 4):
-                s = _fma32(x[4 * m + t], y[4 * m + t], s)
-            quads.append(s)
-        assert orc.dot(x, y) == np.float32(quads[0] + quads[1])
+    for n in (8, 32, 64, 128):
+        for _ in range(40):
+            x = g.standard_normal(n).astype(np.float32)
+            y = g.standard_normal(n).astype(np.float32)
+            blocks = [_chain(x[i:i + 32], y[i:i + 32]) for i in range(0, n, 32)]
+            assert orc.dot(x, y) == orc.tree_sum(np.array(blocks, np.float32))
     # a case where the fused and the separately rounded evaluation differ
     x = np.array([1.0, 1 + 2 ** -12, 0, 0], np.float32)
     y = np.array([-1.0, 1 + 2 ** -12, 0, 0], np.float32)
     fused = np.float32(Fraction(float(x[1])) ** 2 - 1)
     assert orc.dot(x, y) == fused
     assert fused != np.float32(np.float32(x[1] * y[1]) - np.float32(1.0))
+    # one chain over 64 terms and two chains of 32 added differ: after 2^24 every +1 of a single
+    # chain is a tie that rounds back to 2^24, while the second block sums its 32 ones exactly
+    x = np.zeros(64, np.float32)
+    x[0] = 2.0 ** 24
+    x[32:] = 1.0
+    y = np.ones(64, np.float32)
+    assert _chain(x, y) == np.float32(2.0 ** 24)
+    assert orc.dot(x, y) == np.float32(2.0 ** 24 + 32)
 
 
 def test_sums_within_error_bound(orc):
@@ -49,7 +60,8 @@ def test_sums_within_error_bound(orc):
             x = g.standard_normal(n).astype(np.float32)
             y = g.standard_normal(n).astype(np.float32)
             exact = float(sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x, y)))
-            bound = (np.log2(n) + 4) * u * float(np.sum(np.abs(x.astype(np.float64) * y)))
+            depth = min(n, 32) + max(0, int(np.log2(n / 32)))
+            bound = depth * u * float(np.sum(np.abs(x.astype(np.float64) * y)))
             assert abs(float(orc.dot(x, y)) - exact) <= bound
             ex = float(sum(Fraction(float(a)) for a in x))
             assert abs(float(orc.tree_sum(x)) - ex) <= np.log2(n) * u * float(np.sum(np.abs(x)))
