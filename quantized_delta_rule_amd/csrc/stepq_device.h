@@ -477,16 +477,17 @@ __device__ __forceinline__ void store_out(const StepArgs& A, long long tile, int
   if (w == 0) sfor<G>([&](auto gg) { A.out[tile * D + G * lane + CI(gg)] = o[CI(gg)]; });
 }
 
-// Split-mode hand-over of the update factors: a_i, beta k_i per row (lane L < 32 of each
-// wave, written as soon as they are loaded); per column (wave 0, after the readout) either e_j
-// (UV false: GDN, or any gate decaying the rows first) or u_j and v_j (UV true: per-row gate
-// applied after the delta update, e_ij = v_j - a_i u_j).
-template <int D>
+// Split-mode hand-over of the update factors, [4 D] floats per tile: the gate at [0, D) (KDA:
+// a_i per row; GDN: the tile's one alpha at [0]), beta k_i per row at [D, 2 D) (lane L < 32 of
+// each wave, written as soon as they are loaded); per column (wave 0, after the readout) either
+// e_j at [2 D, 3 D) (UV false: GDN, or any gate decaying the rows first) or u_j and v_j at
+// [2 D, 4 D) (UV true: per-row gate applied after the delta update, e_ij = v_j - a_i u_j).
+template <int D, bool KDA>
 __device__ __forceinline__ void put_stash_rows(const StepArgs& A, long long tile, int lane,
                                                int row, float a_row, float bk_row) {
   float* st = A.stash + tile * 4 * D;
   if (lane < 32) {
-    st[row] = a_row;
+    if (KDA || row == 0) st[KDA ? row : 0] = a_row;
     st[D + row] = bk_row;
   }
 }
@@ -575,7 +576,7 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
   }
   if constexpr (MODE == WRITE) {
     const float* st = A.stash + tile * 4 * D;
-    a = st[row];
+    if constexpr (KDA) a = st[row];  // GDN: alpha, read from st[0] above
     bk = st[D + row];
   }
   if constexpr (kRead) bk = beta * kk;
@@ -663,7 +664,7 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
   float a_row, bk_row;
   load_inputs<D, MODE, false>(A, sm, tile, h, lane, row, MODE != ENCODE ? rblk : nullptr, alpha,
                               vv, e, u, a_row, bk_row);
-  if constexpr (MODE == READ) put_stash_rows<D>(A, tile, lane, row, a_row, bk_row);
+  if constexpr (MODE == READ) put_stash_rows<D, false>(A, tile, lane, row, a_row, bk_row);
   wave_lds_sync();
 
   if constexpr (MODE == ENCODE) {
@@ -776,7 +777,7 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, long long s
   }
   float a_row, bk_row;
   load_inputs<D, MODE, false>(A, sm, tile, h, lane, row, nullptr, alpha, vv, e, u, a_row, bk_row);
-  if constexpr (MODE == READ) put_stash_rows<D>(A, tile, lane, row, a_row, bk_row);
+  if constexpr (MODE == READ) put_stash_rows<D, false>(A, tile, lane, row, a_row, bk_row);
   wave_lds_sync();
   if constexpr (MODE != ENCODE) {
     if constexpr (kRead) {
@@ -876,7 +877,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
   float a_row, bk_row;
   load_inputs<D, MODE, true, kUV>(A, sm, tile, h, lane, row, MODE != ENCODE ? rblk : nullptr,
                                   alpha, vv, e, u, a_row, bk_row);
-  if constexpr (MODE == READ) put_stash_rows<D>(A, tile, lane, row, a_row, bk_row);
+  if constexpr (MODE == READ) put_stash_rows<D, true>(A, tile, lane, row, a_row, bk_row);
   if constexpr (MODE != ENCODE) {
     sfor<kStageIt>([&](auto ii) {
       const int x = tid + CI(ii) * NT;
