@@ -392,7 +392,15 @@ def main():
     if "copy_ceiling_GBps" in config:
         roof["frac_of_copy_ceiling"] = roof["achieved"] / config["copy_ceiling_GBps"]
     sq = committed(SQ_COUNTERS, w)
-    if sq is not None:
+    if sq is not None and run.multi:
+        # split mode: the readout and writeback kernels' VALU wave-instructions of one step
+        # over the issue capacity of the step's host-clock time
+        roof["valu_insts_per_step"] = sq["sq_insts_valu_per_step"]
+        roof["valu_issue_frac"] = sq["sq_insts_valu_per_step"] / (step_ms * 1e-3 *
+                                                                  PEAK_VALU_WAVE_INSTS)
+        roof["valu_lane_ops_per_entry"] = sq["sq_insts_valu_per_step"] * 64 / sq["entries"]
+        roof["valu_lane_ops_per_entry_by_kernel"] = sq["lane_ops_per_entry_by_kernel"]
+    elif sq is not None:
         # vector-ALU issue: measured VALU wave-instructions per launch (SQ_INSTS_VALU) over the
         # issue capacity of the launch's duration
         roof["valu_insts_per_launch"] = sq["sq_insts_valu_per_launch"]
