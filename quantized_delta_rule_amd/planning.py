@@ -170,19 +170,19 @@ def code_bytes(w: synth.Workload, plan: "stepq.Plan") -> int:
     return w.B * total
 
 
-# Algorithmic ALU operations per state entry of one decode step, counted from the evaluation
-# order of the method (each binary32 multiply, add, fused multiply-add, maximum, rounding, clamp,
-# conversion and code extraction/insertion counts one; reductions over 128 rows cost
+# Algorithmic ALU operations per state entry of one decode step, counted from the binary32
+# evaluation order the kernels follow (each multiply, add, fused multiply-add, maximum, rounding,
+# clamp, conversion and code extraction/insertion counts one; reductions over 128 rows cost
 # 128 leaves + 31 tree additions per column):
-#   dequantize 3 (extract, convert, x c_j) | k^T S 1.242 | update 2 | q^T S 1.242
-#   row magnitude 0.992 | y = S / r 1 | column maximum 1 (KDA: 2, the per-row 1/qmax)
-#   first quantization 1 | least-squares sums 3.484 | final quantization, clamp, pack 3
-# KDA adds one per entry for its per-row e = v - a_i u.  FP16 pivot rows: convert 1, k^T S,
-# update, q^T S, row magnitude, convert back 1.  Per-row and per-column work (factors and their
-# reciprocals) adds about 0.1 per entry.
-OPS_QUANT_GDN = 3 + 1.242 + 2 + 1.242 + 0.992 + 1 + 1 + 1 + 3.484 + 3 + 0.1
+#   dequantize 3 (extract, convert, x c_j) | k^T S 1.242 | update 1 (T = fma(K_i, e_j, X))
+#   q^T S 1.242 | row magnitude 0.992 | y = T rho_i 1 | column maximum 1 (KDA: 2, the per-row
+#   1/qmax) | first quantization 1 | least-squares sums 3.484 | final quantization, clamp, pack 3
+# KDA adds one per entry for its per-row error e_ij = v_j - a_i u_j.  FP16 pivot rows: convert 1,
+# k^T S, update, q^T S, row magnitude, convert back 1.  Per-row and per-column work (factors and
+# their reciprocals) adds about 0.1 per entry.
+OPS_QUANT_GDN = 3 + 1.242 + 1 + 1.242 + 0.992 + 1 + 1 + 1 + 3.484 + 3 + 0.1
 OPS_QUANT_KDA = OPS_QUANT_GDN + 2
-OPS_PIVOT = 1 + 1.242 + 2 + 1.242 + 0.992 + 1 + 0.1
+OPS_PIVOT = 1 + 1.242 + 1 + 1.242 + 0.992 + 1 + 0.1
 
 
 def algorithmic_ops(w: synth.Workload, plan: "stepq.Plan") -> float:
