@@ -529,11 +529,11 @@ __device__ __forceinline__ void load_state(const StepArgs& A, long long tile, in
 // 2^-72 (its state is erased) or whose factor is 0 -- the key-projection coefficient k f, or
 // k M when the gate decays the rows before the delta update (plan order 1), and the readout
 // coefficient q M.  Encoding: M = 1.
-template <int D, int MODE, bool KDA, bool UV = KDA, typename SM>
+template <int D, int MODE, bool KDA, bool UV = KDA, typename SM, typename Mid>
 __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long tile, int h,
                                             int lane, int row, const uint16_t* rblk,
                                             float& alpha, float* vv, float* e, float* u,
-                                            float& a_row, float& bk_row) {
+                                            float& a_row, float& bk_row, Mid&& mid) {
   constexpr bool kWrite = MODE != READ;
   constexpr int G = Geo<D>::G;
   constexpr bool kRead = MODE == FUSED || MODE == READ;
@@ -579,6 +579,12 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
     if constexpr (KDA) a = st[row];  // GDN: alpha, read from st[0] above
     bk = st[D + row];
   }
+  // the caller's own loads go out behind these (the fences keep the scheduler from hoisting
+  // them): the arithmetic below then waits for the small inputs only, while the caller's
+  // (larger) loads are still in flight
+  __builtin_amdgcn_sched_barrier(0);
+  mid();
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (kRead) bk = beta * kk;
   a_row = a;
   bk_row = bk;
@@ -654,16 +660,19 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
   uint32_t wd[WPW];
   float alpha = 0.0f;
 
-  // ---- phase 0: code loads first (they stream from HBM), then the small per-tile inputs
-  if constexpr (MODE != ENCODE) {
-    sfor<WPW>([&](auto xx) {
-      wd[CI(xx)] = __builtin_nontemporal_load(&wl[CI(xx) * 64]);
-    });
-    sfor<G>([&](auto gg) { cc[CI(gg)] = h2f(cblk[G * lane + CI(gg)]); });
-  }
+  // ---- phase 0: the small per-tile inputs, then the code words (issued before the inputs'
+  // arithmetic, so the decode below waits for each word only as it reaches it)
   float a_row, bk_row;
   load_inputs<D, MODE, false>(A, sm, tile, h, lane, row, MODE != ENCODE ? rblk : nullptr, alpha,
-                              vv, e, u, a_row, bk_row);
+                              vv, e, u, a_row, bk_row, [&] {
+    if constexpr (MODE != ENCODE) {
+      sfor<G>([&](auto gg) { cc[CI(gg)] = h2f(cblk[G * lane + CI(gg)]); });
+      __builtin_amdgcn_sched_barrier(0);  // the column factors ahead of the first code word
+      sfor<WPW>([&](auto xx) {
+        wd[CI(xx)] = __builtin_nontemporal_load(&wl[CI(xx) * 64]);
+      });
+    }
+  });
   if constexpr (MODE == READ) put_stash_rows<D, false>(A, tile, lane, row, a_row, bk_row);
   wave_lds_sync();
 
@@ -776,7 +785,8 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, long long s
     });
   }
   float a_row, bk_row;
-  load_inputs<D, MODE, false>(A, sm, tile, h, lane, row, nullptr, alpha, vv, e, u, a_row, bk_row);
+  load_inputs<D, MODE, false>(A, sm, tile, h, lane, row, nullptr, alpha, vv, e, u, a_row, bk_row,
+                              [] {});
   if constexpr (MODE == READ) put_stash_rows<D, false>(A, tile, lane, row, a_row, bk_row);
   wave_lds_sync();
   if constexpr (MODE != ENCODE) {
@@ -876,7 +886,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
   }
   float a_row, bk_row;
   load_inputs<D, MODE, true, kUV>(A, sm, tile, h, lane, row, MODE != ENCODE ? rblk : nullptr,
-                                  alpha, vv, e, u, a_row, bk_row);
+                                  alpha, vv, e, u, a_row, bk_row, [] {});
   if constexpr (MODE == READ) put_stash_rows<D, true>(A, tile, lane, row, a_row, bk_row);
   if constexpr (MODE != ENCODE) {
     sfor<kStageIt>([&](auto ii) {
