@@ -910,12 +910,20 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
       sfor<8>([&](auto tt) { ms[CI(tt)] = gm[r0 + CI(tt)]; });
       int any = 0;  // sign bit set: the group holds a pivot row
       sfor<8>([&](auto tt) { any |= ms[CI(tt)]; });
+      // every row's two stream words are read before any row is decoded: one LDS wait per group
+      // instead of one per row (a pivot row's low field is its pivot index, below d, so its
+      // unused read stays inside the staging block)
+      uint32_t lo[8], hi[8];
+      sfor<8>([&](auto tt) {
+        const uint32_t* const src = &sm.kc.code[(meta_low(ms[CI(tt)]) >> 5) * 64 + lane];
+        lo[CI(tt)] = src[0];
+        hi[CI(tt)] = src[64];
+      });
+      __builtin_amdgcn_sched_barrier(0);
       auto decode = [&](auto tt) {
         constexpr int t = CI(tt), r = r0 + t;
         const int bw = meta_bits(ms[t]), p = meta_low(ms[t]);
-        const uint32_t lo = sm.kc.code[(p >> 5) * 64 + lane];
-        const uint32_t hi = sm.kc.code[((p >> 5) + 1) * 64 + lane];
-        const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, p & 31);
+        const uint32_t x = __builtin_amdgcn_alignbit(hi[t], lo[t], p & 31);
         sfor<G>([&](auto gg) {
           constexpr int g = CI(gg);
           const int z = __builtin_amdgcn_sbfe((int)x, g * bw, bw);
