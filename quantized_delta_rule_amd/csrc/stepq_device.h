@@ -201,6 +201,7 @@ struct Smem {
     CodeKda<D, KDA> kc;      // used only before and after the transpose
   };
   static_assert(!KDA || kKdaQ + D <= kTr, "KDA staging overflows the transpose area");
+  static_assert(!KDA || RO || kKdaQ + 3 * D <= kTr, "KDA column statistics overflow");
 };
 static_assert(sizeof(Smem<128, false>) <= 40960 && sizeof(Smem<128, true>) <= 40960,
               "four workgroups per CU need at most 40 KB of LDS each");
@@ -246,6 +247,39 @@ __device__ __forceinline__ int get_code(const uint32_t* wd) {
     uint32_t x = __builtin_amdgcn_alignbit(wd[wi + 1], wd[wi], o);
     return __builtin_amdgcn_sbfe((int)x, 0, BITS);
   }
+}
+
+// Decode of 2- and 4-bit codes through byte conversions: each variant m_v of a word holds one
+// code of every byte in that byte's top BITS bits with zeros below (a shift and a mask per
+// variant), so converting a sign-extended byte (the compiler's sub-dword conversion) gives
+// z * 2^(8 - BITS) in one instruction; times c * 2^(BITS - 8) that is c z exactly (c is a
+// widened binary16, so the power-of-two scaling is exact).  Against extract + convert per code
+// this saves about 0.6 instructions per code.  The byte is taken by a cast to int8_t, not by
+// __builtin_amdgcn_sbfe: on a masked word this LLVM turned the signed conversion of the sbfe
+// result into an unsigned one (uitofp of a value that can be negative), which decodes every
+// negative code wrong.
+template <int BITS, int G, int WPW>
+__device__ __forceinline__ void decode_narrow(const uint32_t* wd, const float* cc,
+                                              float (&S)[32][G]) {
+  constexpr int NV = 8 / BITS;  // codes per byte
+  constexpr uint32_t kTop = BITS == 4 ? 0xF0F0F0F0u : 0xC0C0C0C0u;
+  constexpr float kScale = BITS == 4 ? 0x1p-4f : 0x1p-6f;
+  float cs[G];
+  sfor<G>([&](auto gg) { cs[CI(gg)] = cc[CI(gg)] * kScale; });
+  sfor<WPW>([&](auto xx) {
+    constexpr int x = CI(xx);
+    uint32_t m[NV];
+    sfor<NV>([&](auto vv) {
+      constexpr int sh = 8 - BITS - CI(vv) * BITS;
+      m[CI(vv)] = (sh ? wd[x] << sh : wd[x]) & kTop;
+    });
+    sfor<32 / BITS>([&](auto kk) {
+      constexpr int K = x * (32 / BITS) + CI(kk);
+      constexpr int r = K / G, g = K % G;
+      constexpr int o = (K * BITS) % 32, byte = o / 8, v = (o % 8) / BITS;
+      S[r][g] = cs[g] * (float)(int)(int8_t)(m[v] >> (8 * byte));
+    });
+  });
 }
 
 // Appends code K (low BITS bits of f) to the lane's stream kept in acc, newest bits on top, and
@@ -356,18 +390,42 @@ __device__ __forceinline__ void xwave_max_put(SM& sm, int w, int lane, const flo
   float* const dst = lds_pin(sm, max_slot<D>(sm, w) + G * lane);
   sfor<G>([&](auto gg) { dst[CI(gg)] = x[CI(gg)]; });
 }
+
+// Per-column statistics once per tile: wave g < G finishes column G*lane + g of every lane (one
+// column per lane, instead of all G columns in every wave) and shares the result through LDS:
+// GDN in wave 0's section past its maximum slot (that section's transpose is done by then), KDA
+// just past the rows' q (dead after the readout).  [0, D): 1/c0; [D, 2D): 1/c_hat.
 template <int D, typename SM>
-__device__ __forceinline__ void xwave_max(SM& sm, int lane, float* x) {
+__device__ __forceinline__ float* col_share(SM& sm) {
+  return lds_pin(sm, sm.tr + (SM::kKDA ? SM::kKdaQ + D : D));
+}
+// maximum of the waves' partial maxima of column G*lane + g
+template <int D, typename SM>
+__device__ __forceinline__ float xwave_max_col(SM& sm, int lane, int g) {
   constexpr int G = Geo<D>::G, NW = Geo<D>::NW;
-  // wave w' partials sit at a constant distance from wave 0's
-  const float* const p0 = lds_pin(sm, max_slot<D>(sm, 0) + G * lane);
-  constexpr int kStride = SM::kKDA ? D : SM::kSec;
-  sfor<G>([&](auto gg) {
-    constexpr int g = CI(gg);
-    float m = p0[g];
-    sfor<NW - 1>([&](auto ww) { m = __builtin_fmaxf(m, p0[(CI(ww) + 1) * kStride + g]); });
-    x[g] = m;
-  });
+  constexpr int kStride = SM::kKDA ? D : SM::kSec;  // between the waves' partials
+  const float* const p0 = lds_pin(sm, max_slot<D>(sm, 0) + G * lane) + g;
+  float m = p0[0];
+  sfor<NW - 1>([&](auto ww) { m = __builtin_fmaxf(m, p0[(CI(ww) + 1) * kStride]); });
+  return m;
+}
+// pairwise tree over the waves' partials of column G*lane + g (the order xwave_sum uses)
+template <int D, typename SM>
+__device__ __forceinline__ float xwave_sum_col(SM& sm, int slot, int lane, int g) {
+  constexpr int G = Geo<D>::G, NW = Geo<D>::NW;
+  const float* const p = lds_pin(sm, &sm.red[slot][0][G * lane]) + g;
+  if constexpr (NW == 2) return p[0] + p[D];
+  else return (p[0] + p[D]) + (p[2 * D] + p[3 * D]);
+}
+// Column factor of one column from its least-squares sums (c0 when sq is not positive), stored
+// at cdst (unless null); returns 1/c_hat (0 if dead).
+__device__ __forceinline__ float col_factor1(float num, float sq, float c0, uint16_t* cdst,
+                                             unsigned& fl) {
+  const float c1 = sq > 0.0f ? num / sq : c0;
+  const uint16_t ch = f2h(c1);
+  if (is_inf16(ch)) fl |= kFlagScaleOvf;
+  if (cdst) *cdst = ch;
+  return rcp16(h2f(ch));
 }
 
 // |S| partial sums of each row over this lane's columns, transposed through LDS.
@@ -455,20 +513,6 @@ __device__ __forceinline__ void ls_sums(const float (&S)[32][G], const RW& rows,
   });
 }
 
-// Column factor from the least-squares sums; wave 0 stores it; returns 1/c_hat (0 if dead).
-template <int G>
-__device__ __forceinline__ void col_factor(const float* num, const float* sq, const float* c0,
-                                           int w, int lane, uint16_t* cblk, float* ic,
-                                           unsigned& fl) {
-  sfor<G>([&](auto gg) {
-    constexpr int g = CI(gg);
-    const float c1 = sq[g] > 0.0f ? num[g] / sq[g] : c0[g];
-    const uint16_t ch = f2h(c1);
-    if (is_inf16(ch)) fl |= kFlagScaleOvf;
-    if (w == 0 && cblk) cblk[G * lane + g] = ch;
-    ic[g] = rcp16(h2f(ch));
-  });
-}
 
 template <int D>
 __device__ __forceinline__ void store_out(const StepArgs& A, long long tile, int w, int lane,
@@ -680,13 +724,17 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
     load_state<D>(A, tile, row0, lane, S);
   } else {
     // ---- phase 1: dequantize, and u = S_hat^T k
-    sfor<R>([&](auto rr) {
-      constexpr int r = CI(rr);
-      sfor<G>([&](auto gg) {
-        constexpr int g = CI(gg);
-        S[r][g] = cc[g] * (float)get_code<BITS, r * G + g>(wd);
+    if constexpr (BITS <= 4) {
+      decode_narrow<BITS, G, WPW>(wd, cc, S);
+    } else {
+      sfor<R>([&](auto rr) {
+        constexpr int r = CI(rr);
+        sfor<G>([&](auto gg) {
+          constexpr int g = CI(gg);
+          S[r][g] = cc[g] * (float)get_code<BITS, r * G + g>(wd);
+        });
       });
-    });
+    }
     if constexpr (kRead) {
       row_dot<G>(S, [&](int r) { return rows.r[r].kr; }, u);
       xwave_put<D>(sm, 0, w, lane, u);
@@ -725,22 +773,28 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
     scale_rows<G>(S, rows, mx);
     xwave_max_put<D>(sm, w, lane, mx);
     __syncthreads();
-    xwave_max<D>(sm, lane, mx);
-    float c0[G], ic0[G];
-    sfor<G>([&](auto gg) {
-      c0[CI(gg)] = mx[CI(gg)] * IQ;
-      ic0[CI(gg)] = rcp0(c0[CI(gg)]);
-    });
+    float* const csh = col_share<D>(sm);
+    float c0w = 0.0f;  // c0 of column G*lane + w (waves w < G)
+    if (w < G) {
+      c0w = xwave_max_col<D>(sm, lane, w) * IQ;
+      csh[G * lane + w] = rcp0(c0w);
+    }
+    __syncthreads();
+    float ic0[G];
+    sfor<G>([&](auto gg) { ic0[CI(gg)] = csh[G * lane + CI(gg)]; });
 
     // ---- phase 4: first quantization and the least-squares column refit
     float num[G], sq[G], ic[G];
     ls_sums<G>(S, rows, ic0, num, sq);
     xwave_put<D>(sm, 0, w, lane, num);  // slot 0 (u) and slot 1 (readout) were last read
-    xwave_put<D>(sm, 1, w, lane, sq);   // before the barrier above
+    xwave_put<D>(sm, 1, w, lane, sq);   // before the barriers above
     __syncthreads();
-    xwave_sum<D>(sm, 0, lane, num);
-    xwave_sum<D>(sm, 1, lane, sq);
-    col_factor<G>(num, sq, c0, w, lane, cblk, ic, fl);
+    if (w < G) {
+      const float n = xwave_sum_col<D>(sm, 0, lane, w), q = xwave_sum_col<D>(sm, 1, lane, w);
+      csh[D + G * lane + w] = col_factor1(n, q, c0w, cblk ? cblk + G * lane + w : nullptr, fl);
+    }
+    __syncthreads();
+    sfor<G>([&](auto gg) { ic[CI(gg)] = csh[D + G * lane + CI(gg)]; });
 
     // ---- phase 5: final requantization and packing
     uint32_t acc = 0;
@@ -1034,12 +1088,15 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     });
     xwave_max_put<D>(sm, w, lane, mx);
     __syncthreads();  // also orders the zeroing above before the packing below
-    xwave_max<D>(sm, lane, mx);
-    float c0[G], ic0[G];
-    sfor<G>([&](auto gg) {
-      c0[CI(gg)] = mx[CI(gg)];
-      ic0[CI(gg)] = rcp0(mx[CI(gg)]);
-    });
+    float* const csh = col_share<D>(sm);
+    float c0w = 0.0f;  // c0 of column G*lane + w (waves w < G)
+    if (w < G) {
+      c0w = xwave_max_col<D>(sm, lane, w);
+      csh[G * lane + w] = rcp0(c0w);
+    }
+    __syncthreads();
+    float ic0[G];
+    sfor<G>([&](auto gg) { ic0[CI(gg)] = csh[G * lane + CI(gg)]; });
 
     // ---- phase 4: z0 and least-squares sums
     float num[G], sq[G], ic[G];
@@ -1047,9 +1104,12 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     xwave_put<D>(sm, 0, w, lane, num);
     xwave_put<D>(sm, 1, w, lane, sq);
     __syncthreads();
-    xwave_sum<D>(sm, 0, lane, num);
-    xwave_sum<D>(sm, 1, lane, sq);
-    col_factor<G>(num, sq, c0, w, lane, cblk, ic, fl);
+    if (w < G) {
+      const float n = xwave_sum_col<D>(sm, 0, lane, w), q = xwave_sum_col<D>(sm, 1, lane, w);
+      csh[D + G * lane + w] = col_factor1(n, q, c0w, cblk ? cblk + G * lane + w : nullptr, fl);
+    }
+    __syncthreads();
+    sfor<G>([&](auto gg) { ic[CI(gg)] = csh[D + G * lane + CI(gg)]; });
 
     // ---- phase 5: requantize and pack into the zeroed LDS stream, then copy out.  A row's G
     // codes (G * b bits) land at its uniform stream position: OR-ed into one word, or two when
