@@ -91,6 +91,14 @@ __device__ __forceinline__ float rcp16(float x) {
 
 __device__ __forceinline__ bool is_inf16(uint16_t h) { return (h & 0x7FFFu) == 0x7C00u; }
 
+// fma(a, b, kMagic) as one v_fmaak_f32 (the constant rides in the instruction).  In the KDA
+// packing loop the compiler otherwise materializes kMagic with a v_mov before every fma.
+__device__ __forceinline__ float fma_magic(float a, float b) {
+  float d;
+  asm("v_fmaak_f32 %0, %1, %2, 0x4b400000" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
 // code offset by kMagic: fma rounds the exact product y*ic once; then clamp to +-qm
 __device__ __forceinline__ float quant_off(float y, float ic, float qm) {
   return __builtin_amdgcn_fmed3f(__builtin_fmaf(y, ic, kMagic), kMagic - qm, kMagic + qm);
@@ -166,11 +174,14 @@ __device__ __forceinline__ KConst<T>* opaque_s(KConst<T>* p) {
 }
 
 // Per-row layout metadata of mixed-width tiles, packed by the plan into one int: a pivot row is
-// 0x80000000 | (its index in the pivot block); a quantized row is its stream bit position |
-// (width << 16).  Read once per row and phase as a wave-uniform scalar.
+// 0x80000000 | (its index in the pivot block); a quantized row is its stream bit position
+// (bits 0..15) | width << 16 | (its G codes cross a word boundary) << 20 | qmax << 24.  Read once
+// per row and phase as a wave-uniform scalar.
 __device__ __forceinline__ bool meta_pivot(int m) { return m < 0; }
 __device__ __forceinline__ int meta_low(int m) { return m & 0xFFFF; }  // pivot index / position
 __device__ __forceinline__ int meta_bits(int m) { return (m >> 16) & 15; }
+__device__ __forceinline__ bool meta_straddles(int m) { return (m >> 20) & 1; }
+__device__ __forceinline__ int meta_qmax(int m) { return (m >> 24) & 0x7F; }
 template <int D, bool KDA>
 struct CodeKda {  // code block staging of mixed-width tiles
   uint32_t code[(2 * D * 8 / 32 + 1) * 64];
@@ -201,7 +212,8 @@ struct Smem {
     CodeKda<D, KDA> kc;      // used only before and after the transpose
   };
   static_assert(!KDA || kKdaQ + D <= kTr, "KDA staging overflows the transpose area");
-  static_assert(!KDA || RO || kKdaQ + 3 * D <= kTr, "KDA column statistics overflow");
+  static_assert(!KDA || RO || kKdaQ + 4 * D <= kTr, "KDA column statistics overflow");
+  static_assert(KDA || RO || D + 3 * D <= kSec, "GDN column statistics overflow wave 0's section");
 };
 static_assert(sizeof(Smem<128, false>) <= 40960 && sizeof(Smem<128, true>) <= 40960,
               "four workgroups per CU need at most 40 KB of LDS each");
@@ -394,7 +406,8 @@ __device__ __forceinline__ void xwave_max_put(SM& sm, int w, int lane, const flo
 // Per-column statistics once per tile: wave g < G finishes column G*lane + g of every lane (one
 // column per lane, instead of all G columns in every wave) and shares the result through LDS:
 // GDN in wave 0's section past its maximum slot (that section's transpose is done by then), KDA
-// just past the rows' q (dead after the readout).  [0, D): 1/c0; [D, 2D): 1/c_hat.
+// just past the rows' q (dead after the readout).  [0, D): 1/c0; [D, 2D): 1/c_hat; then the
+// binary16 c_hat of the D columns.
 template <int D, typename SM>
 __device__ __forceinline__ float* col_share(SM& sm) {
   return lds_pin(sm, sm.tr + (SM::kKDA ? SM::kKdaQ + D : D));
@@ -417,15 +430,39 @@ __device__ __forceinline__ float xwave_sum_col(SM& sm, int slot, int lane, int g
   if constexpr (NW == 2) return p[0] + p[D];
   else return (p[0] + p[D]) + (p[2 * D] + p[3 * D]);
 }
-// Column factor of one column from its least-squares sums (c0 when sq is not positive), stored
-// at cdst (unless null); returns 1/c_hat (0 if dead).
-__device__ __forceinline__ float col_factor1(float num, float sq, float c0, uint16_t* cdst,
+// Column factor of one column from its least-squares sums (c0 when sq is not positive): its
+// binary16 value in ch; returns 1/c_hat (0 if dead).
+__device__ __forceinline__ float col_factor1(float num, float sq, float c0, uint16_t& ch,
                                              unsigned& fl) {
   const float c1 = sq > 0.0f ? num / sq : c0;
-  const uint16_t ch = f2h(c1);
+  ch = f2h(c1);
   if (is_inf16(ch)) fl |= kFlagScaleOvf;
-  if (cdst) *cdst = ch;
   return rcp16(h2f(ch));
+}
+// The refit once the least-squares partial sums are staged: waves g < G finish column
+// G*lane + g, every wave then reads 1/c_hat of its G columns, and wave 0 stores the lane's G
+// binary16 factors with one store (cblk may be null), so each segment's factor block is written
+// by whole words.
+template <int D, typename SM>
+__device__ __forceinline__ void col_refit(SM& sm, float* csh, int w, int lane, float c0w,
+                                          uint16_t* cblk, float* ic, unsigned& fl) {
+  constexpr int G = Geo<D>::G;
+  uint16_t* const chs = reinterpret_cast<uint16_t*>(csh + 2 * D);
+  if (w < G) {
+    const float n = xwave_sum_col<D>(sm, 0, lane, w), q = xwave_sum_col<D>(sm, 1, lane, w);
+    uint16_t ch;
+    csh[D + G * lane + w] = col_factor1(n, q, c0w, ch, fl);
+    chs[G * lane + w] = ch;
+  }
+  __syncthreads();
+  sfor<G>([&](auto gg) { ic[CI(gg)] = csh[D + G * lane + CI(gg)]; });
+  if (w == 0 && cblk) {
+    if constexpr (G == 2) {
+      reinterpret_cast<uint32_t*>(cblk)[lane] = reinterpret_cast<const uint32_t*>(chs)[lane];
+    } else {
+      cblk[lane] = chs[lane];
+    }
+  }
 }
 
 // |S| partial sums of each row over this lane's columns, transposed through LDS.
@@ -789,12 +826,7 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
     xwave_put<D>(sm, 0, w, lane, num);  // slot 0 (u) and slot 1 (readout) were last read
     xwave_put<D>(sm, 1, w, lane, sq);   // before the barriers above
     __syncthreads();
-    if (w < G) {
-      const float n = xwave_sum_col<D>(sm, 0, lane, w), q = xwave_sum_col<D>(sm, 1, lane, w);
-      csh[D + G * lane + w] = col_factor1(n, q, c0w, cblk ? cblk + G * lane + w : nullptr, fl);
-    }
-    __syncthreads();
-    sfor<G>([&](auto gg) { ic[CI(gg)] = csh[D + G * lane + CI(gg)]; });
+    col_refit<D>(sm, csh, w, lane, c0w, cblk, ic, fl);
 
     // ---- phase 5: final requantization and packing
     uint32_t acc = 0;
@@ -1104,12 +1136,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     xwave_put<D>(sm, 0, w, lane, num);
     xwave_put<D>(sm, 1, w, lane, sq);
     __syncthreads();
-    if (w < G) {
-      const float n = xwave_sum_col<D>(sm, 0, lane, w), q = xwave_sum_col<D>(sm, 1, lane, w);
-      csh[D + G * lane + w] = col_factor1(n, q, c0w, cblk ? cblk + G * lane + w : nullptr, fl);
-    }
-    __syncthreads();
-    sfor<G>([&](auto gg) { ic[CI(gg)] = csh[D + G * lane + CI(gg)]; });
+    col_refit<D>(sm, csh, w, lane, c0w, cblk, ic, fl);
 
     // ---- phase 5: requantize and pack into the zeroed LDS stream, then copy out.  A row's G
     // codes (G * b bits) land at its uniform stream position: OR-ed into one word, or two when
@@ -1125,22 +1152,20 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
         constexpr int r = r0 + CI(tt);
         const int m = ms[CI(tt)];
         if (!meta_pivot(m)) {
-          const int bw = meta_bits(m), p = meta_low(m);
-          const int qmi = (1 << (bw - 1)) - 1;
+          const int bw = meta_bits(m), p = meta_low(m), qmi = meta_qmax(m);
           const float lo_b = __builtin_bit_cast(float, 0x4B400000 - qmi);
           const float hi_b = __builtin_bit_cast(float, 0x4B400000 + qmi);
           const uint32_t mask = (1u << bw) - 1u;
           uint32_t wv = 0;
           sfor<G>([&](auto gg) {
             constexpr int g = CI(gg);
-            const float t = __builtin_amdgcn_fmed3f(__builtin_fmaf(S[r][g], ic[g], kMagic), lo_b,
-                                                    hi_b);
+            const float t = __builtin_amdgcn_fmed3f(fma_magic(S[r][g], ic[g]), lo_b, hi_b);
             wv |= (__builtin_bit_cast(uint32_t, t) & mask) << (g * bw);
           });
           const int sh = p & 31;
           uint32_t* const dst = &sm.kc.code[(p >> 5) * 64 + lane];
           atomicOr(dst, wv << sh);
-          if (sh + G * bw > 32) atomicOr(dst + 64, wv >> (32 - sh));
+          if (meta_straddles(m)) atomicOr(dst + 64, wv >> (32 - sh));
         }
       });
     });

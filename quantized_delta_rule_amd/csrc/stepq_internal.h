@@ -37,6 +37,7 @@ struct DevPlan {
   const int* rowpos;         // [H*d] stream bit offset of the row's first code (-1 on pivots)
   const int* pividx;         // [H*d] row index inside the pivot block (-1 otherwise)
   const int* rowmeta;        // [H*d] packed: pivot 0x80000000 | pividx, else rowpos | bits << 16
+                             //   | (codes cross a word boundary) << 20 | qmax << 24
   unsigned* status;          // accumulated STEPQ_FLAG_* bits
 };
 
