@@ -129,7 +129,8 @@ hipError_t wait_writeback(stepq_plan* p, hipStream_t stream) {
   return hipSuccess;
 }
 
-// One workgroup per (request, head): B * n_heads must fit the launch grid's x dimension.
+// One workgroup per (request, head) on a (B, n_heads) grid; the tile count B * n_heads is kept
+// below INT_MAX (tile indices and the split-mode hand-over size are computed from it).
 int check_grid(const stepq_plan* p, int B) {
   if ((long long)B * p->H > INT_MAX)
     return fail(STEPQ_ERR_INVALID_ARG, "B * n_heads = %lld exceeds the launch grid",
@@ -161,6 +162,8 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   if (d->kind != STEPQ_KIND_GDN && d->kind != STEPQ_KIND_KDA)
     return fail(STEPQ_ERR_INVALID_ARG, "kind must be STEPQ_KIND_GDN or STEPQ_KIND_KDA");
   if (d->n_heads < 1) return fail(STEPQ_ERR_INVALID_ARG, "n_heads must be >= 1");
+  // the step kernels' launch grid is (requests, heads): heads are its second dimension
+  if (d->n_heads > 65535) return fail(STEPQ_ERR_INVALID_ARG, "n_heads must be <= 65535");
   if (d->d_k != d->d_v) return fail(STEPQ_ERR_UNSUPPORTED, "this build supports d_k == d_v only");
   if (d->d_k != 64 && d->d_k != 128)
     return fail(STEPQ_ERR_UNSUPPORTED, "d_k must be 64 or 128 (got %d)", d->d_k);

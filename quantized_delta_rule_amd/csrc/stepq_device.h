@@ -1207,12 +1207,13 @@ __device__ __forceinline__ long long pool_slot(const StepArgs& A, int b, int h) 
   return valid ? s : -1;
 }
 
-// Workgroup j runs head head_order[j / B] of request j % B: heads are dispatched in the plan's
-// order (longest tiles first, FP16 pivot heads last), which shortens the launch's ragged end.
+// Grid (B, H): workgroup (b, j) runs head head_order[j] of request b, the requests of one head
+// dispatched together and the heads in the plan's order (longest tiles first, FP16 pivot heads
+// last), which shortens the launch's ragged end.  The two grid indices need no division.
 template <int D, int MODE>
 __global__ __launch_bounds__(Geo<D>::NT, MODE == READ ? 5 : 4) void k_gdn(StepArgs A) {
   __shared__ Smem<D, false, MODE == READ> sm;
-  const int hs = blockIdx.x / A.B, b = blockIdx.x - hs * A.B;
+  const int hs = blockIdx.y, b = blockIdx.x;
   const int h = kread(A.P.head_order, hs);
   const long long slot = pool_slot<MODE>(A, b, h);
   if (slot < 0) return;
@@ -1235,8 +1236,7 @@ __global__ __launch_bounds__(Geo<D>::NT, MODE == READ ? 5 : 4) void k_gdn(StepAr
 template <int D, int MODE>
 __global__ __launch_bounds__(Geo<D>::NT, MODE == READ ? 5 : 4) void k_kda(StepArgs A) {
   __shared__ Smem<D, true, MODE == READ> sm;
-  const int tile = blockIdx.x;
-  const int b = tile / A.P.H, h = tile - b * A.P.H;
+  const int b = blockIdx.x, h = blockIdx.y;  // grid (B, H)
   const long long slot = pool_slot<MODE>(A, b, h);
   if (slot < 0) return;
   if (A.P.order) kda_tile<D, MODE, 1>(A, b, slot, h, sm);
@@ -1287,7 +1287,7 @@ __global__ __launch_bounds__(D) void k_unpack(DevPlan P, const uint8_t* pool, fl
 
 template <int D, int KIND>
 hipError_t launch_kind(Mode mode, const StepArgs& a, hipStream_t s) {
-  const dim3 grid(a.B * a.P.H), block(Geo<D>::NT);
+  const dim3 grid(a.B, a.P.H), block(Geo<D>::NT);
   switch (mode) {
     case FUSED:
       if constexpr (KIND == 0) hipLaunchKernelGGL((k_gdn<D, FUSED>), grid, block, 0, s, a);

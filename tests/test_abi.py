@@ -42,7 +42,7 @@ def _desc(sq, **kw):
 
 
 @pytest.mark.parametrize("case", ["bits", "omega_nan", "omega_neg", "gdn_mixed", "gdn_partial_pivot",
-                                  "d96", "pivot2", "order"])
+                                  "d96", "pivot2", "order", "heads"])
 def test_invalid_plans_are_rejected(sq, case):
     H, d = 2, 128
     bits = np.full((H, d), 6, np.int8)
@@ -63,11 +63,18 @@ def test_invalid_plans_are_rejected(sq, case):
         bits, piv, om = bits[:, :96], piv[:, :96], om[:, :96]
     elif case == "pivot2":
         piv[0, 0] = 2
+    elif case == "heads":  # the launch grid's second dimension holds the heads
+        H, d = 65536, 64
+        bits = np.full((H, d), 6, np.int8)
+        piv = np.zeros((H, d), np.uint8)
+        om = np.ones((H, d), np.float32)
     order = 2 if case == "order" else 0
     with pytest.raises(sq.StepqError) as ei:
         sq.Plan(kind, bits, piv, om, order=order)
     msg = str(ei.value)
     assert "(-1)" in msg or "(-2)" in msg, msg
+    if case == "heads":
+        assert "n_heads must be <= 65535" in msg, msg
 
 
 def test_kda_allows_mixed_rows_until_the_device_check(sq):
