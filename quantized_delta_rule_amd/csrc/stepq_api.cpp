@@ -213,8 +213,9 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
       } else {
         pividx[r] = -1;
         rowpos[r] = (int)lane_bits;
-        // stream position | width | the row's G codes cross a word boundary | qmax
-        rowmeta[r] = (int)lane_bits | (hb[i] << 16) |
+        // bit offset in its first word | that word's index << 8 | width | the row's G codes
+        // cross a word boundary | qmax
+        rowmeta[r] = (int)(lane_bits & 31) | (int)((lane_bits >> 5) << 8) | (hb[i] << 16) |
                      ((int)((lane_bits & 31) + G * hb[i] > 32) << 20) |
                      (((1 << (hb[i] - 1)) - 1) << 24);
         bits[r] = hb[i];

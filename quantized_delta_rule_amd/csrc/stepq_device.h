@@ -174,11 +174,15 @@ __device__ __forceinline__ KConst<T>* opaque_s(KConst<T>* p) {
 }
 
 // Per-row layout metadata of mixed-width tiles, packed by the plan into one int: a pivot row is
-// 0x80000000 | (its index in the pivot block); a quantized row is its stream bit position
-// (bits 0..15) | width << 16 | (its G codes cross a word boundary) << 20 | qmax << 24.  Read once
-// per row and phase as a wave-uniform scalar.
+// 0x80000000 | (its index in the pivot block); a quantized row is the bit offset of its first
+// code in its first stream word (bits 0..4) | that word's index << 8 | width << 16 | (its G
+// codes cross a word boundary) << 20 | qmax << 24.  Read once per row and phase as a
+// wave-uniform scalar; the word index arrives ready as a byte offset into the [word][lane]
+// staging (word * 256), and shifts use the low five bits as they are.
 __device__ __forceinline__ bool meta_pivot(int m) { return m < 0; }
-__device__ __forceinline__ int meta_low(int m) { return m & 0xFFFF; }  // pivot index / position
+__device__ __forceinline__ int meta_pividx(int m) { return m & 0xFF; }
+__device__ __forceinline__ int meta_shift(int m) { return m & 31; }
+__device__ __forceinline__ int meta_lds(int m) { return m & 0x3F00; }  // word * 256 (0: pivot)
 __device__ __forceinline__ int meta_bits(int m) { return (m >> 16) & 15; }
 __device__ __forceinline__ bool meta_straddles(int m) { return (m >> 20) & 1; }
 __device__ __forceinline__ int meta_qmax(int m) { return (m >> 24) & 0x7F; }
@@ -997,19 +1001,20 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
       int any = 0;  // sign bit set: the group holds a pivot row
       sfor<8>([&](auto tt) { any |= ms[CI(tt)]; });
       // every row's two stream words are read before any row is decoded: one LDS wait per group
-      // instead of one per row (a pivot row's low field is its pivot index, below d, so its
-      // unused read stays inside the staging block)
+      // instead of one per row (a pivot row reads the block's first words and does not use them)
       uint32_t lo[8], hi[8];
+      const char* const lane_words = reinterpret_cast<const char*>(&sm.kc.code[lane]);
       sfor<8>([&](auto tt) {
-        const uint32_t* const src = &sm.kc.code[(meta_low(ms[CI(tt)]) >> 5) * 64 + lane];
+        const uint32_t* const src =
+            reinterpret_cast<const uint32_t*>(lane_words + meta_lds(ms[CI(tt)]));
         lo[CI(tt)] = src[0];
         hi[CI(tt)] = src[64];
       });
       __builtin_amdgcn_sched_barrier(0);
       auto decode = [&](auto tt) {
         constexpr int t = CI(tt), r = r0 + t;
-        const int bw = meta_bits(ms[t]), p = meta_low(ms[t]);
-        const uint32_t x = __builtin_amdgcn_alignbit(hi[t], lo[t], p & 31);
+        const int bw = meta_bits(ms[t]);
+        const uint32_t x = __builtin_amdgcn_alignbit(hi[t], lo[t], meta_shift(ms[t]));
         sfor<G>([&](auto gg) {
           constexpr int g = CI(gg);
           const int z = __builtin_amdgcn_sbfe((int)x, g * bw, bw);
@@ -1022,7 +1027,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
         sfor<8>([&](auto tt) {
           constexpr int t = CI(tt), r = r0 + t;
           if (meta_pivot(ms[t])) {
-            const int pv = meta_low(ms[t]);
+            const int pv = meta_pividx(ms[t]);
             sfor<G>([&](auto gg) { S[r][CI(gg)] = h2f(pblk[pv * D + G * lane + CI(gg)]); });
           } else {
             decode(tt);
@@ -1098,7 +1103,7 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
         sfor<8>([&](auto tt) {
           constexpr int r = r0 + CI(tt);
           if (meta_pivot(ms[CI(tt)])) {
-            const int pv = meta_low(ms[CI(tt)]);
+            const int pv = meta_pividx(ms[CI(tt)]);
             const float M = rows.r[r].M;
             sfor<G>([&](auto gg) {
               const uint16_t hv = f2h(S[r][CI(gg)] * M);
@@ -1143,31 +1148,38 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     // they straddle a word boundary; words shared with a neighbouring wave's rows combine the
     // same way.  The clamp bounds +-qmax in the offset domain are the integers 0x4B400000 +-
     // qmax read as binary32 (the grid spacing there is 1).
+    char* const lane_words = reinterpret_cast<char*>(&sm.kc.code[lane]);
     sfor<R / 8>([&](auto qq) {
       constexpr int r0 = 8 * CI(qq);
       int ms[8];
       KConst<int>* const gm = opaque_s(gmeta);
       sfor<8>([&](auto tt) { ms[CI(tt)] = gm[r0 + CI(tt)]; });
-      sfor<8>([&](auto tt) {
+      int any = 0;  // sign bit set: the group holds a pivot row
+      sfor<8>([&](auto tt) { any |= ms[CI(tt)]; });
+      auto pack = [&](auto tt) {
         constexpr int r = r0 + CI(tt);
         const int m = ms[CI(tt)];
-        if (!meta_pivot(m)) {
-          const int bw = meta_bits(m), p = meta_low(m), qmi = meta_qmax(m);
-          const float lo_b = __builtin_bit_cast(float, 0x4B400000 - qmi);
-          const float hi_b = __builtin_bit_cast(float, 0x4B400000 + qmi);
-          const uint32_t mask = (1u << bw) - 1u;
-          uint32_t wv = 0;
-          sfor<G>([&](auto gg) {
-            constexpr int g = CI(gg);
-            const float t = __builtin_amdgcn_fmed3f(fma_magic(S[r][g], ic[g]), lo_b, hi_b);
-            wv |= (__builtin_bit_cast(uint32_t, t) & mask) << (g * bw);
-          });
-          const int sh = p & 31;
-          uint32_t* const dst = &sm.kc.code[(p >> 5) * 64 + lane];
-          atomicOr(dst, wv << sh);
-          if (meta_straddles(m)) atomicOr(dst + 64, wv >> (32 - sh));
-        }
-      });
+        const int bw = meta_bits(m), qmi = meta_qmax(m);
+        const float lo_b = __builtin_bit_cast(float, 0x4B400000 - qmi);
+        const float hi_b = __builtin_bit_cast(float, 0x4B400000 | qmi);
+        const uint32_t mask = (1u << bw) - 1u;
+        uint32_t wv = 0;
+        sfor<G>([&](auto gg) {
+          constexpr int g = CI(gg);
+          const float t = __builtin_amdgcn_fmed3f(fma_magic(S[r][g], ic[g]), lo_b, hi_b);
+          wv |= (__builtin_bit_cast(uint32_t, t) & mask) << (g * bw);
+        });
+        uint32_t* const dst = reinterpret_cast<uint32_t*>(lane_words + meta_lds(m));
+        atomicOr(dst, wv << meta_shift(m));
+        if (meta_straddles(m)) atomicOr(dst + 64, wv >> (32 - meta_shift(m)));
+      };
+      if (!meta_pivot(any)) {
+        sfor<8>(pack);
+      } else {
+        sfor<8>([&](auto tt) {
+          if (!meta_pivot(ms[CI(tt)])) pack(tt);
+        });
+      }
     });
     __syncthreads();
     {

@@ -36,8 +36,9 @@ struct DevPlan {
   const int* bits;           // [H*d] width (0 on pivot rows)
   const int* rowpos;         // [H*d] stream bit offset of the row's first code (-1 on pivots)
   const int* pividx;         // [H*d] row index inside the pivot block (-1 otherwise)
-  const int* rowmeta;        // [H*d] packed: pivot 0x80000000 | pividx, else rowpos | bits << 16
-                             //   | (codes cross a word boundary) << 20 | qmax << 24
+  const int* rowmeta;        // [H*d] packed: pivot 0x80000000 | pividx, else rowpos & 31 |
+                             //   (rowpos >> 5) << 8 | bits << 16 | (codes cross a word
+                             //   boundary) << 20 | qmax << 24
   unsigned* status;          // accumulated STEPQ_FLAG_* bits
 };
 
