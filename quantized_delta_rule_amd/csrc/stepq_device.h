@@ -140,17 +140,17 @@ struct Geo {
 //   K    (beta k) / M: the update T = fma(K, e, X)
 //   M    row scale of the updated state S = M T
 //   rho  M / r_hat (after the row factor; 0 on pivot and dead rows): y = T rho
-//   W    omega r_hat^2
+//   W    omega r_hat^2 (before the row factor: omega, or -1 on a KDA pivot row)
+//   qm   readout coefficient q M
 template <bool KDA>
 struct Row;
 template <>
 struct Row<false> {
-  float kr, K, qm, M, rho, W;  // qm: readout coefficient q M
+  float kr, K, qm, M, rho, W;
 };
 template <>
 struct Row<true> {
-  float kr, K, a, M, rho, W;   // the gate a; q M is kept in the staging area
-  int meta;                    // packed width, stream position or pivot index (row_meta)
+  float kr, K, qm, M, rho, W, a;  // a: the row's gate
 };
 
 // Read-only data in the constant address space: loads at wave-uniform addresses become scalar
@@ -195,28 +195,27 @@ struct CodeKda<D, false> {};
 
 // Both tile kinds fit in 40 KB, so four workgroups fit in a CU's 160 KB.  Only two cross-wave
 // slots: GDN column maxima pass through each wave's own (by then dead) transpose section; KDA
-// keeps them, and the rows' q, in the transpose area just past its code staging block (q is
-// dead after the readout barrier, before the transpose; the maxima come after it).
-// RO (the split mode's readout kernels) keeps only what a readout uses -- no transpose area,
-// and for KDA the code staging block and q -- so five workgroups fit per CU.
+// keeps them in the transpose area just past its code staging block (they come after the
+// transposes).  RO (the split mode's readout kernels) keeps only what a readout uses -- no
+// transpose area, and for KDA the code staging block -- so five workgroups fit per CU.
 template <int D, bool KDA, bool RO = false>
 struct Smem {
   static constexpr int NW = Geo<D>::NW;
   static constexpr bool kKDA = KDA;
   static constexpr int NSLOT = 2;
   static constexpr int kSec = 32 * 65;  // one wave's transpose section [row][lane], +1 pad
-  // KDA: column-maximum slots [NW][D] and the rows' q [D], after the code staging block
+  // KDA: column-maximum slots [NW][D] after the code staging block, then the column statistics
   static constexpr int kKdaMax = KDA ? (int)(sizeof(CodeKda<D, KDA>) / sizeof(float)) : 0;
-  static constexpr int kKdaQ = kKdaMax + NW * D;
-  static constexpr int kTr = !RO ? NW * kSec : KDA ? kKdaQ + D : 1;
+  static constexpr int kKdaCol = kKdaMax + NW * D;
+  static constexpr int kTr = !RO ? NW * kSec : KDA ? kKdaMax : 1;
   Row<KDA> row[D];
   float red[NSLOT][NW][D];
   union {
     float tr[kTr];           // the waves' transpose sections (conflict-free), q, KDA maxima
     CodeKda<D, KDA> kc;      // used only before and after the transpose
   };
-  static_assert(!KDA || kKdaQ + D <= kTr, "KDA staging overflows the transpose area");
-  static_assert(!KDA || RO || kKdaQ + 4 * D <= kTr, "KDA column statistics overflow");
+  static_assert(!KDA || kKdaMax <= kTr, "KDA staging overflows the transpose area");
+  static_assert(!KDA || RO || kKdaCol + 3 * D <= kTr, "KDA column statistics overflow");
   static_assert(KDA || RO || D + 3 * D <= kSec, "GDN column statistics overflow wave 0's section");
 };
 static_assert(sizeof(Smem<128, false>) <= 40960 && sizeof(Smem<128, true>) <= 40960,
@@ -410,11 +409,11 @@ __device__ __forceinline__ void xwave_max_put(SM& sm, int w, int lane, const flo
 // Per-column statistics once per tile: wave g < G finishes column G*lane + g of every lane (one
 // column per lane, instead of all G columns in every wave) and shares the result through LDS:
 // GDN in wave 0's section past its maximum slot (that section's transpose is done by then), KDA
-// just past the rows' q (dead after the readout).  [0, D): 1/c0; [D, 2D): 1/c_hat; then the
+// past the maximum slots (in wave 2's section, whose transposes are done by then).  [0, D): 1/c0; [D, 2D): 1/c_hat; then the
 // binary16 c_hat of the D columns.
 template <int D, typename SM>
 __device__ __forceinline__ float* col_share(SM& sm) {
-  return lds_pin(sm, sm.tr + (SM::kKDA ? SM::kKdaQ + D : D));
+  return lds_pin(sm, sm.tr + (SM::kKDA ? SM::kKdaCol : D));
 }
 // maximum of the waves' partial maxima of column G*lane + g
 template <int D, typename SM>
@@ -555,11 +554,12 @@ __device__ __forceinline__ void ls_sums(const float (&S)[32][G], const RW& rows,
 }
 
 
+// The readout of the lane's G columns, stored by one wave (`mine`).
 template <int D>
-__device__ __forceinline__ void store_out(const StepArgs& A, long long tile, int w, int lane,
+__device__ __forceinline__ void store_out(const StepArgs& A, long long tile, bool mine, int lane,
                                           const float* o) {
   constexpr int G = Geo<D>::G;
-  if (w == 0) sfor<G>([&](auto gg) { A.out[tile * D + G * lane + CI(gg)] = o[CI(gg)]; });
+  if (mine) sfor<G>([&](auto gg) { A.out[tile * D + G * lane + CI(gg)] = o[CI(gg)]; });
 }
 
 // Split-mode hand-over of the update factors, [4 D] floats per tile: the gate at [0, D) (KDA:
@@ -677,12 +677,9 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
     auto& rec = sm.row[row];
     // row factor: r_hat of a quantized row; 1 on pivot rows and FP16 pivot heads
     const float rf = rblk && !(KDA && meta_pivot(meta)) ? h2f(rh) : 1.0f;
-    if constexpr (KDA) {
-      rec.meta = meta;
-      rec.a = a;
-    }
+    if constexpr (KDA) rec.a = a;
     rec.rho = iden;
-    rec.W = om;
+    rec.W = KDA && meta_pivot(meta) ? -1.0f : om;  // omega >= 0 (or -0) on every other row
     if constexpr (MODE == ENCODE) {
       rec.M = 1.0f;
     } else {
@@ -693,8 +690,7 @@ __device__ __forceinline__ void load_inputs(const StepArgs& A, SM& sm, long long
       rec.K = flat ? 1.0f : bk / m;
       if constexpr (kRead) {
         rec.kr = A.P.order ? kk * m : kk * rf;
-        if constexpr (KDA) sm.tr[SM::kKdaQ + row] = qv * Mv;
-        else rec.qm = qv * Mv;
+        rec.qm = qv * Mv;
       }
     }
   }
@@ -793,13 +789,15 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
       float o[G];
       row_dot<G>(S, [&](int r) { return rows.r[r].qm; }, o);
       xwave_put<D>(sm, 1, w, lane, o);
-      __syncthreads();
-      xwave_sum<D>(sm, 1, lane, o);
-      store_out<D>(A, tile, w, lane, o);
       if constexpr (MODE == READ) {
+        __syncthreads();
+        xwave_sum<D>(sm, 1, lane, o);
+        store_out<D>(A, tile, w == 0, lane, o);
         put_stash_cols<D, false>(A, tile, w, lane, e, u, vv);
         return;
       }
+      // the fused step adds the waves' readout partials after the column-maximum barrier below
+      // (slot 1 is next written after the barrier that follows that one)
     }
   }
   if constexpr (kWrite) {
@@ -819,6 +817,15 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
     if (w < G) {
       c0w = xwave_max_col<D>(sm, lane, w) * IQ;
       csh[G * lane + w] = rcp0(c0w);
+    }
+    if constexpr (kRead) {
+      // the fused step's readout, by the last wave (one that finishes no column statistics)
+      static_assert(Gm::NW - 1 >= G, "the readout wave must not be a column-statistics wave");
+      if (w == Gm::NW - 1) {
+        float o[G];
+        xwave_sum<D>(sm, 1, lane, o);
+        store_out<D>(A, tile, true, lane, o);
+      }
     }
     __syncthreads();
     float ic0[G];
@@ -899,7 +906,7 @@ __device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, long long s
       xwave_put<D>(sm, 1, w, lane, o);
       __syncthreads();
       xwave_sum<D>(sm, 1, lane, o);
-      store_out<D>(A, tile, w, lane, o);
+      store_out<D>(A, tile, w == 0, lane, o);
       if constexpr (MODE == READ) {
         put_stash_cols<D, false>(A, tile, w, lane, e, u, vv);
         return;
@@ -1061,24 +1068,33 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     });
     if constexpr (kRead) {
       float o[G];
-      const float* const qk = lds_pin(sm, sm.tr + SM::kKdaQ + row0);
-      row_dot<G>(S, [&](int r) { return qk[r]; }, o);
+      row_dot<G>(S, [&](int r) { return rows.r[r].qm; }, o);
       xwave_put<D>(sm, 1, w, lane, o);
-      __syncthreads();
-      xwave_sum<D>(sm, 1, lane, o);
-      store_out<D>(A, tile, w, lane, o);
       if constexpr (MODE == READ) {
+        __syncthreads();
+        xwave_sum<D>(sm, 1, lane, o);
+        store_out<D>(A, tile, w == 0, lane, o);
         put_stash_cols<D, kUV>(A, tile, w, lane, e, u, vv);
         return;
       }
+      // the fused step adds the waves' readout partials after the next barrier (slot 1 is next
+      // written after the column-maximum barrier)
     }
   }
   if constexpr (kWrite) {
     put_rowabs<D>(sm, S, lane);
     wave_lds_sync();
-    const bool piv = meta_pivot(sm.row[row].meta);
+    const bool piv = sm.row[row].W < 0.0f;
     row_factor<D>(sm, lane, row, piv, rblk, fl);
     __syncthreads();  // every wave's transposes are done: zero the code staging for packing
+    if constexpr (kRead) {
+      // the fused step's readout, by the last wave
+      if (w == Gm::NW - 1) {
+        float o[G];
+        xwave_sum<D>(sm, 1, lane, o);
+        store_out<D>(A, tile, true, lane, o);
+      }
+    }
     {
       const int n4 = nwords * 16;
       u32x4* l4 = reinterpret_cast<u32x4*>(sm.kc.code);
