@@ -63,5 +63,38 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+KERNEL_SOURCES = ("stepq_k128_gdn.hip", "stepq_k128_kda.hip", "stepq_k64.hip")
+
+
+def kernel_resources() -> dict:
+    """Compiles the step kernels' units for the device only and returns the compiler's resource
+    report per kernel: {mangled name: {"VGPRs", "ScratchSize", "Occupancy", "VGPRs Spill",
+    "SGPRs Spill", "LDS Size"}} (integers)."""
+    import re
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    flags = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    with tempfile.TemporaryDirectory() as td:
+        def one(src):
+            return _run([hipcc, *flags, *inc, "--cuda-device-only", "-c",
+                         "-Rpass-analysis=kernel-resource-usage", os.path.join(CSRC, src),
+                         "-o", os.path.join(td, src + ".o")])
+        with ThreadPoolExecutor(len(KERNEL_SOURCES)) as ex:
+            text = "\n".join(ex.map(one, KERNEL_SOURCES))
+    out, cur = {}, None
+    for line in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+(VGPRs|ScratchSize|Occupancy|VGPRs Spill|SGPRs Spill|LDS Size)"
+                      r"(?: \[[^]]*\])?: (\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1)] = int(m.group(2))
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -491,8 +491,10 @@ template <int D, typename SM>
 __device__ __forceinline__ void row_factor(SM& sm, int lane, int row, bool piv, uint16_t* rblk,
                                            unsigned& fl) {
   float lv[6];
+  // the lane index is re-read here rather than kept live from the tile's start
+  const int lt = opaque((int)threadIdx.x);
   const float* const src = lds_pin(
-      sm, sm.tr + (threadIdx.x >> 6) * SM::kSec + (lane & 31) * 65 + (lane & 32));
+      sm, sm.tr + (lt >> 6) * SM::kSec + (lt & 31) * 65 + (lt & 32));
   sfor<32>([&](auto jj) { tree_push<CI(jj)>(lv, src[CI(jj)]); });
   const float other = __shfl_xor(lv[5], 32);
   const float Mr = sm.row[row].M;
