@@ -129,8 +129,6 @@ struct Geo {
   static constexpr int R = 32;        // rows per wave
   static constexpr int NW = D / R;    // waves per tile
   static constexpr int NT = 64 * NW;  // threads per tile
-  static constexpr int NQ = R / 4;    // fma chains of four per column and wave
-  static constexpr int TOP = 3;       // tree level holding a wave's partial (log2 NQ)
 };
 
 // Per-row record, read at wave-uniform addresses (broadcast reads).  One interleaved record per
