@@ -391,7 +391,8 @@ __device__ __forceinline__ void xwave_sum(SM& sm, int slot, int lane, float* x) 
   });
 }
 // Column maxima across waves: GDN tiles stage them in each wave's own transpose section (dead
-// once that wave's row factors are done), KDA tiles in cross-wave slot 2.
+// once that wave's row factors are done), KDA tiles in the transpose area just past the code
+// staging block (in wave 2's section: stored after the barrier that ends every transpose).
 template <int D, typename SM>
 __device__ __forceinline__ float* max_slot(SM& sm, int w) {
   if constexpr (SM::kKDA) return sm.tr + SM::kKdaMax + w * D;
@@ -407,7 +408,7 @@ __device__ __forceinline__ void xwave_max_put(SM& sm, int w, int lane, const flo
 // Per-column statistics once per tile: wave g < G finishes column G*lane + g of every lane (one
 // column per lane, instead of all G columns in every wave) and shares the result through LDS:
 // GDN in wave 0's section past its maximum slot (that section's transpose is done by then), KDA
-// past the maximum slots (in wave 2's section, whose transposes are done by then).  [0, D): 1/c0; [D, 2D): 1/c_hat; then the
+// past the maximum slots (also in wave 2's section).  [0, D): 1/c0; [D, 2D): 1/c_hat; then the
 // binary16 c_hat of the D columns.
 template <int D, typename SM>
 __device__ __forceinline__ float* col_share(SM& sm) {
