@@ -2,7 +2,10 @@
 mode, per-head (GDN) or per-row (KDA) widths from {2, 4, 6, 8}, FP16 pivot heads or rows (none,
 a few, many, or a whole head), contrast geometry.  Each plan encodes an oracle warm-up state and
 runs two decode steps; every tile of every step must match the oracle (codes bit-exact up to the
-documented .5-boundary exemption, readouts within rel L2 1e-4)."""
+documented .5-boundary exemption, readouts within rel L2 1e-4).  STEPQ_RANDOM_PLANS sets the
+number of plans (default 48) for a longer sweep."""
+import os
+
 import numpy as np
 import pytest
 
@@ -11,7 +14,7 @@ from quantized_delta_rule_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-N_PLANS = 48
+N_PLANS = int(os.environ.get("STEPQ_RANDOM_PLANS", "48"))
 
 
 @pytest.fixture(scope="module")
