@@ -262,6 +262,11 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   };
   std::stable_sort(head_order.begin(), head_order.end(),
                    [&](int x, int y) { return rank(x) > rank(y); });
+  std::vector<HeadDisp> disp(H);
+  for (int j = 0; j < H; j++) {
+    const int h = head_order[j];
+    disp[j] = HeadDisp{head_off[h], h, head_type[h], off_r[h], off_c[h], {0, 0}};
+  }
 
   auto* p = new (std::nothrow) stepq_plan();
   if (!p) return fail(STEPQ_ERR_OOM, "host allocation failed");
@@ -293,6 +298,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   const size_t i_hoff = add(head_off.data(), H * sizeof(long long));
   const size_t i_type = add(head_type.data(), H * sizeof(int));
   const size_t i_hord = add(head_order.data(), H * sizeof(int));
+  const size_t i_disp = add(disp.data(), H * sizeof(HeadDisp));
   const size_t i_opiv = add(off_piv.data(), H * sizeof(int));
   const size_t i_or = add(off_r.data(), H * sizeof(int));
   const size_t i_oc = add(off_c.data(), H * sizeof(int));
@@ -327,6 +333,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   dp.head_off = (const long long*)at(i_hoff);
   dp.head_type = (const int*)at(i_type);
   dp.head_order = (const int*)at(i_hord);
+  dp.disp = (const HeadDisp*)at(i_disp);
   dp.off_piv = (const int*)at(i_opiv);
   dp.off_r = (const int*)at(i_or);
   dp.off_c = (const int*)at(i_oc);

@@ -162,6 +162,18 @@ __device__ __forceinline__ T kread(const T* p, long long i) {
   return ((KConst<T>*)p)[i];
 }
 
+// Dispatch position j's record (one scalar load of its fields).
+__device__ __forceinline__ HeadDisp kread_disp(KConst<HeadDisp>* p, int j) {
+  KConst<int>* const q = (KConst<int>*)(p + j);
+  HeadDisp r;
+  r.off = *(KConst<long long>*)q;
+  r.h = q[2];
+  r.type = q[3];
+  r.off_r = q[4];
+  r.off_c = q[5];
+  return r;
+}
+
 // The same uniform pointer, made opaque to the optimizer: loads through it are not merged with
 // loads of the same data elsewhere (which would keep them live, in scalar registers, across
 // phases).
@@ -719,7 +731,8 @@ __device__ __forceinline__ void erase_rows(float (&S)[32][G], uint64_t mask) {
 // ---------------------------------------------------------------------------------------------
 
 template <int D, int MODE, int BITS, typename SM>
-__device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slot, int h, SM& sm) {
+__device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slot,
+                                         const HeadDisp& hd, SM& sm) {
   using Gm = Geo<D>;
   constexpr int G = Gm::G, R = Gm::R;
   constexpr int WPW = R * G * BITS / 32;  // code words per lane for one wave's rows
@@ -728,12 +741,13 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
   constexpr bool kRead = MODE == FUSED || MODE == READ;   // computes u and the readout
   constexpr bool kWrite = MODE != READ;                   // refits and packs
   const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
+  const int h = hd.h;
   const long long tile = (long long)b * A.P.H + h;
-  uint8_t* seg = A.pool + slot * A.P.bpr + kread(A.P.head_off, h);
+  uint8_t* seg = A.pool + slot * A.P.bpr + hd.off;
   // this lane's code words: word x of the wave's rows at wl[64 x] (one base, immediate offsets)
   uint32_t* const wl = reinterpret_cast<uint32_t*>(seg) + (w * WPW * 64 + lane);
-  uint16_t* rblk = reinterpret_cast<uint16_t*>(seg + kread(A.P.off_r, h));
-  uint16_t* cblk = reinterpret_cast<uint16_t*>(seg + kread(A.P.off_c, h));
+  uint16_t* rblk = reinterpret_cast<uint16_t*>(seg + hd.off_r);
+  uint16_t* cblk = reinterpret_cast<uint16_t*>(seg + hd.off_c);
   const Rows<SM> rows(sm);
   unsigned fl = 0;
 
@@ -858,14 +872,16 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
 // ---------------------------------------------------------------------------------------------
 
 template <int D, int MODE, typename SM>
-__device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, long long slot, int h, SM& sm) {
+__device__ __forceinline__ void pivot_tile(const StepArgs& A, int b, long long slot,
+                                           const HeadDisp& hd, SM& sm) {
   using Gm = Geo<D>;
   constexpr int G = Gm::G, R = Gm::R;
   constexpr bool kRead = MODE == FUSED || MODE == READ;
   constexpr bool kWrite = MODE != READ;
   const int lane = threadIdx.x & 63, w = wave_id(), row0 = w * R, row = row0 + (lane & 31);
+  const int h = hd.h;
   const long long tile = (long long)b * A.P.H + h;
-  uint8_t* seg = A.pool + slot * A.P.bpr + kread(A.P.head_off, h);
+  uint8_t* seg = A.pool + slot * A.P.bpr + hd.off;
   uint16_t* hblk = reinterpret_cast<uint16_t*>(seg);
   const Rows<SM> rows(sm);
   unsigned fl = 0;
@@ -1238,27 +1254,30 @@ __device__ __forceinline__ long long pool_slot(const StepArgs& A, int b, int h) 
 
 // Grid (B, H): workgroup (b, j) runs head head_order[j] of request b, the requests of one head
 // dispatched together and the heads in the plan's order (longest tiles first, FP16 pivot heads
-// last), which shortens the launch's ragged end.  The two grid indices need no division.
+// last), which shortens the launch's ragged end.  The two grid indices need no division, and
+// the dispatch position's record gives the head, its type and its segment layout at once.
 template <int D, int MODE>
 __global__ __launch_bounds__(Geo<D>::NT, MODE == READ ? 5 : 4) void k_gdn(StepArgs A) {
   __shared__ Smem<D, false, MODE == READ> sm;
   const int hs = blockIdx.y, b = blockIdx.x;
-  const int h = kread(A.P.head_order, hs);
-  const long long slot = pool_slot<MODE>(A, b, h);
+  const HeadDisp hd = kread_disp((KConst<HeadDisp>*)A.P.disp, hs);
+  const long long slot = pool_slot<MODE>(A, b, hd.h);
   if (slot < 0) return;
   // Each tile path reads the arguments it uses itself, through an opaque pointer to the kernel
   // argument segment: argument values shared by several paths are then not loaded once before
   // the switch and held live across it (which spilled about 20 scalar registers per tile).
+  // The dispatch record is re-read the same way (a scalar-cache hit by then).
   auto args = [&]() -> const StepArgs& {
     KConst<StepArgs>* const p = (KConst<StepArgs>*)__builtin_amdgcn_kernarg_segment_ptr();
     return *(const StepArgs*)opaque_s(p);
   };
-  switch (kread(A.P.head_type, h)) {
-    case 2: gdn_tile<D, MODE, 2>(args(), b, slot, h, sm); break;
-    case 4: gdn_tile<D, MODE, 4>(args(), b, slot, h, sm); break;
-    case 6: gdn_tile<D, MODE, 6>(args(), b, slot, h, sm); break;
-    case 8: gdn_tile<D, MODE, 8>(args(), b, slot, h, sm); break;
-    default: pivot_tile<D, MODE>(args(), b, slot, h, sm); break;
+  auto rec = [&]() { return kread_disp(opaque_s((KConst<HeadDisp>*)args().P.disp), hs); };
+  switch (hd.type) {
+    case 2: gdn_tile<D, MODE, 2>(args(), b, slot, rec(), sm); break;
+    case 4: gdn_tile<D, MODE, 4>(args(), b, slot, rec(), sm); break;
+    case 6: gdn_tile<D, MODE, 6>(args(), b, slot, rec(), sm); break;
+    case 8: gdn_tile<D, MODE, 8>(args(), b, slot, rec(), sm); break;
+    default: pivot_tile<D, MODE>(args(), b, slot, rec(), sm); break;
   }
 }
 

@@ -18,6 +18,19 @@ constexpr int kHeadMixed = -1;
 // ENCODE: refit and pack an fp32 state given in memory.
 enum Mode { FUSED = 0, READ = 1, WRITE = 2, ENCODE = 3 };
 
+// One dispatch position j of the GDN kernels (grid index y): the head head_order[j], its type
+// and its segment layout, so a workgroup finds everything it needs to start loading with one
+// 32-byte scalar load (instead of the head index, then the head's type and offsets).
+struct alignas(32) HeadDisp {
+  long long off;  // segment byte offset inside one request
+  int h;          // the head
+  int type;       // its head_type
+  int off_r;      // row-factor block offset inside the segment
+  int off_c;      // column-factor block offset
+  int pad[2];
+};
+static_assert(sizeof(HeadDisp) == 32, "one 32-byte scalar load per dispatch position");
+
 // Device-resident plan tables (all arrays in device memory; per-row arrays are [H * d]).
 struct DevPlan {
   int H, D;                  // heads, d_k = d_v
@@ -26,6 +39,7 @@ struct DevPlan {
   const long long* head_off; // [H] segment byte offset inside one request
   const int* head_type;      // [H]
   const int* head_order;     // [H] dispatch order of the heads (GDN fused/split/encode kernels)
+  const HeadDisp* disp;      // [H] per dispatch position: head_order[j] and its layout
   const int* off_piv;        // [H] pivot block offset inside the segment
   const int* off_r;          // [H] row-factor block offset
   const int* off_c;          // [H] column-factor block offset
