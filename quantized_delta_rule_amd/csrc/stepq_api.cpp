@@ -296,8 +296,6 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
     return pieces.size() - 1;
   };
   const size_t i_hoff = add(head_off.data(), H * sizeof(long long));
-  const size_t i_type = add(head_type.data(), H * sizeof(int));
-  const size_t i_hord = add(head_order.data(), H * sizeof(int));
   const size_t i_disp = add(disp.data(), H * sizeof(HeadDisp));
   const size_t i_opiv = add(off_piv.data(), H * sizeof(int));
   const size_t i_or = add(off_r.data(), H * sizeof(int));
@@ -331,8 +329,6 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   dp.order = d->order;
   dp.bpr = p->bpr;
   dp.head_off = (const long long*)at(i_hoff);
-  dp.head_type = (const int*)at(i_type);
-  dp.head_order = (const int*)at(i_hord);
   dp.disp = (const HeadDisp*)at(i_disp);
   dp.off_piv = (const int*)at(i_opiv);
   dp.off_r = (const int*)at(i_or);

@@ -18,9 +18,9 @@ constexpr int kHeadMixed = -1;
 // ENCODE: refit and pack an fp32 state given in memory.
 enum Mode { FUSED = 0, READ = 1, WRITE = 2, ENCODE = 3 };
 
-// One dispatch position j of the GDN kernels (grid index y): the head head_order[j], its type
-// and its segment layout, so a workgroup finds everything it needs to start loading with one
-// 32-byte scalar load (instead of the head index, then the head's type and offsets).
+// One dispatch position j of the GDN kernels (grid index y): the j-th head of the plan's
+// dispatch order, its type and its segment layout, so a workgroup finds everything it needs to
+// start loading with one 32-byte scalar load.
 struct alignas(32) HeadDisp {
   long long off;  // segment byte offset inside one request
   int h;          // the head
@@ -37,9 +37,7 @@ struct DevPlan {
   int order;                 // 0: A = Diag(a)(I - beta k k^T); 1: A = (I - beta k k^T) Diag(a)
   long long bpr;             // bytes per request
   const long long* head_off; // [H] segment byte offset inside one request
-  const int* head_type;      // [H]
-  const int* head_order;     // [H] dispatch order of the heads (GDN fused/split/encode kernels)
-  const HeadDisp* disp;      // [H] per dispatch position: head_order[j] and its layout
+  const HeadDisp* disp;      // [H] GDN kernels, per dispatch position: the head and its layout
   const int* off_piv;        // [H] pivot block offset inside the segment
   const int* off_r;          // [H] row-factor block offset
   const int* off_c;          // [H] column-factor block offset
