@@ -458,8 +458,12 @@ def main():
         wx = synth.WORKLOADS[wid]
         log(f"workload {wid} {wx.name}: setup")
         rx = Run(wx, dev, args.inputs)
-        tx = rx.timed(args.steps, args.warmup)
+        # at least 200 timed steps: a short run of a small launch measures the host clock's
+        # bracketing more than the steps
+        nx = max(args.steps, 200)
+        tx = rx.timed(nx, max(args.warmup, 20))
         sx = rx.summary(tx)
+        sx["steps"] = nx
         log(f"workload {wid}: {sx['head_steps_per_s'] / 1e6:.1f} M head-steps/s, "
             f"{sx['us_per_step']:.1f} us/step, HBM frac {sx['hbm_frac']:.3f} "
             f"(setup {rx.setup_s:.0f} s)")

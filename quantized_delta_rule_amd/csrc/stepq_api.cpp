@@ -60,12 +60,22 @@ float tree_sum(const float* x, int n) {
   return tree_sum(x, n / 2) + tree_sum(x + n / 2, n - n / 2);
 }
 
-// Restores the caller's current device on scope exit.
+// Makes the plan's device current and restores the caller's on scope exit; when it is already
+// current (the usual case) no device switch is made either way.
 struct DeviceGuard {
   int prev = -1;
   bool ok_ = false;
   explicit DeviceGuard(int dev) {
-    if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(dev) == hipSuccess) ok_ = true;
+    if (hipGetDevice(&prev) != hipSuccess) {
+      prev = -1;
+      return;
+    }
+    if (prev == dev) {
+      prev = -1;
+      ok_ = true;
+      return;
+    }
+    if (hipSetDevice(dev) == hipSuccess) ok_ = true;
   }
   ~DeviceGuard() {
     if (prev >= 0) (void)hipSetDevice(prev);
