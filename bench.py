@@ -171,7 +171,9 @@ class Run:
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         ev0.record()
-        for i in range(steps):
+        # the rotation continues from the warm-up: a short timed run does not start on the
+        # replicas the warm-up has just left in the Infinity Cache
+        for i in range(warmup, warmup + steps):
             self.run(i)
         ev1.record()
         self.drain()
@@ -367,6 +369,7 @@ def main():
     plan0 = run.units[0][0]
     spare = plan0.alloc_pool(w.B)
     plan0.encode(run.S0_dev, spare, w.B)
+    torch.cuda.synchronize()  # the spare pool's first touch stays outside the timed encodes
     x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     x0.record()
     for _ in range(20):
@@ -404,6 +407,12 @@ def main():
         # clock; the launch-stream figure covers the readout kernels only
         roof["achieved"] = run.alg_bytes / (step_ms * 1e-3) / 1e9
         roof["frac"] = roof["achieved"] / PEAK_HBM_GBS
+    if traffic is not None:
+        # HBM bytes by the committed counters (FETCH_SIZE + WRITE_SIZE, scaled by the copy
+        # calibration) over this run's time of the same launches
+        span_ms = step_ms / run.launches if run.multi else avg_k
+        roof["traffic_GBps"] = traffic / (span_ms * 1e-3) / 1e9
+        roof["traffic_frac"] = roof["traffic_GBps"] / PEAK_HBM_GBS
     if "copy_ceiling_GBps" in config:
         roof["frac_of_copy_ceiling"] = roof["achieved"] / config["copy_ceiling_GBps"]
     sq = committed(SQ_COUNTERS, w)
@@ -464,6 +473,10 @@ def main():
         tx = rx.timed(nx, max(args.warmup, 20))
         sx = rx.summary(tx)
         sx["steps"] = nx
+        cx = committed(COUNTERS, wx)
+        if cx is not None:
+            sx["traffic_frac"] = (cx["hbm_bytes_per_launch"] * rx.launches /
+                                  (tx["step_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS)
         log(f"workload {wid}: {sx['head_steps_per_s'] / 1e6:.1f} M head-steps/s, "
             f"{sx['us_per_step']:.1f} us/step, HBM frac {sx['hbm_frac']:.3f} "
             f"(setup {rx.setup_s:.0f} s)")
