@@ -1182,6 +1182,9 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
     // same way.  The clamp bounds +-qmax in the offset domain are the integers 0x4B400000 +-
     // qmax read as binary32 (the grid spacing there is 1).
     char* const lane_words = reinterpret_cast<char*>(&sm.kc.code[lane]);
+    // a zero the optimizer cannot see: it stays in one register as the low half of every row's
+    // 64-bit shift below (as a known 0 it is rematerialized by a move per row)
+    const uint32_t zero = (uint32_t)opaque(0);
     sfor<R / 8>([&](auto qq) {
       constexpr int r0 = 8 * CI(qq);
       int ms[8];
@@ -1195,16 +1198,20 @@ __device__ __forceinline__ void kda_tile(const StepArgs& A, int b, long long slo
         const int bw = meta_bits(m), qmi = meta_qmax(m);
         const float lo_b = __builtin_bit_cast(float, 0x4B400000 - qmi);
         const float hi_b = __builtin_bit_cast(float, 0x4B400000 | qmi);
-        const uint32_t mask = (1u << bw) - 1u;
-        uint32_t wv = 0;
+        // each code's low bw bits enter at the top of acc (one funnel shift per code, no
+        // mask): after the row's G codes they fill its top G * bw bits, code 0 lowest, zeros
+        // below
+        uint32_t acc = 0;
         sfor<G>([&](auto gg) {
-          constexpr int g = CI(gg);
-          const float t = __builtin_amdgcn_fmed3f(fma_magic(S[r][g], ic[g]), lo_b, hi_b);
-          wv |= (__builtin_bit_cast(uint32_t, t) & mask) << (g * bw);
+          const float t = __builtin_amdgcn_fmed3f(fma_magic(S[r][CI(gg)], ic[CI(gg)]), lo_b, hi_b);
+          acc = __builtin_amdgcn_alignbit(__builtin_bit_cast(uint32_t, t), acc, bw);
         });
+        // one 64-bit shift moves them from the top of the pair (acc, 0) to bit `sh` of their
+        // first stream word; the upper half is what runs into the next word
+        const uint64_t y = (((uint64_t)acc << 32) | zero) >> (64 - G * bw - meta_shift(m));
         uint32_t* const dst = reinterpret_cast<uint32_t*>(lane_words + meta_lds(m));
-        atomicOr(dst, wv << meta_shift(m));
-        if (meta_straddles(m)) atomicOr(dst + 64, wv >> (32 - meta_shift(m)));
+        atomicOr(dst, (uint32_t)y);
+        if (meta_straddles(m)) atomicOr(dst + 64, (uint32_t)(y >> 32));
       };
       if (!meta_pivot(any)) {
         sfor<8>(pack);
