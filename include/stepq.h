@@ -64,7 +64,7 @@ enum { STEPQ_ORDER_DELTA_FIRST = 0, STEPQ_ORDER_DECAY_FIRST = 1 };
  *             width and either all or none of a head's rows are pivots.  STEPQ_KIND_KDA: the
  *             unit is a key row -- widths and pivot flags may vary row by row.
  *   n_heads   heads per request (one layer), 1 .. 65535.
- *   d_k, d_v  state shape; this build supports d_k == d_v in {64, 128}.
+ *   d_k, d_v  state shape; the library supports d_k == d_v in {64, 128}.
  *   bits      [n_heads * d_k] int8, widths in {2, 4, 6, 8} (ignored on pivot rows).
  *   pivot     [n_heads * d_k] uint8, 1 = FP16 pivot row (stored raw, not quantized).
  *   omega     [n_heads * d_k] float, row impact omega_i = E[(A_t^T q_t)_i^2] (Method 2),

@@ -18,7 +18,7 @@ Layout of one head (d_k rows, d_v columns, per-row width b_i and pivot flag):
   c block      d_v binary16 column factors                    -- absent if every row is a pivot
   padding      zero bytes up to a multiple of 256.
 
-The pages fix none of this: it is the layout this build stores (the digest, Method 4, only says
+The pages fix none of this: it is the layout the library stores (the digest, Method 4, only says
 that codes, scale metadata and FP16 pivots are packed back in place).
 """
 from __future__ import annotations

@@ -20,7 +20,7 @@
  * The scale formulas (r_i = (mean_j|S_ij| + 1e-8)/(1 + omega_i/mean omega), c_j initialised to
  * max_i|S_ij/r_i|/qmax, one omega-weighted least-squares refit with z fixed, symmetric
  * round-half-even with qmax = 2^(b-1)-1) and the gate A_t = Diag(a)(I - beta k k^T) are the
- * readings this build takes where the pages leave the step open; the other gate order,
+ * readings taken here where the pages leave the step open; the other gate order,
  * A_t = (I - beta k k^T) Diag(a), is available as a plan option (ORC_DECAY_FIRST).
  *
  * This is one binary32 evaluation order of that step, fixed so that a GPU can follow it bit for

@@ -174,7 +174,7 @@ int stepq_plan_create(const stepq_plan_desc* d, stepq_plan_t* out) {
   if (d->n_heads < 1) return fail(STEPQ_ERR_INVALID_ARG, "n_heads must be >= 1");
   // the step kernels' launch grid is (requests, heads): heads are its second dimension
   if (d->n_heads > 65535) return fail(STEPQ_ERR_INVALID_ARG, "n_heads must be <= 65535");
-  if (d->d_k != d->d_v) return fail(STEPQ_ERR_UNSUPPORTED, "this build supports d_k == d_v only");
+  if (d->d_k != d->d_v) return fail(STEPQ_ERR_UNSUPPORTED, "the library supports d_k == d_v only");
   if (d->d_k != 64 && d->d_k != 128)
     return fail(STEPQ_ERR_UNSUPPORTED, "d_k must be 64 or 128 (got %d)", d->d_k);
   if (!d->bits || !d->pivot || !d->omega)
