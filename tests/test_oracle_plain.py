@@ -362,3 +362,61 @@ def test_check_catches_planted_mistakes(orc, monkeypatch, mistake):
         monkeypatch.setattr(plain, "readout", lambda S, q: real_readout(S.T, q))
     with pytest.raises(PP.PlainMismatch):
         _spec_vs_plain(w, [0, 1, 2, 3], w.steps)
+
+
+# ----------------------------------------------------------------------------------------------
+# the binary16 decision rule of the check itself
+# ----------------------------------------------------------------------------------------------
+
+def _h(x):
+    return np.asarray(np.float16(x)).view(np.uint16)
+
+
+def test_f16_interval_is_the_rounding_interval():
+    lo, hi = PP._f16_interval(np.array([_h(1.0), _h(-1.0), _h(0.0), _h(65504.0)]))
+    assert lo[0] == 1 - 2.0**-12 and hi[0] == 1 + 2.0**-11
+    assert lo[1] == -(1 + 2.0**-11) and hi[1] == -(1 - 2.0**-12)
+    assert lo[2] == -(2.0**-25) and hi[2] == 2.0**-25
+    assert hi[3] == 65520.0
+    # every binary16 value's interval holds the value and fl16 maps its inner points back
+    h = np.arange(1, 0x7C00, 97, dtype=np.uint16)  # (0: its lower half rounds to -0)
+    lo, hi = PP._f16_interval(h)
+    v = h.view(np.float16).astype(np.float64)
+    assert np.all(lo < v) and np.all(v < hi)
+    inner = np.concatenate([0.999 * lo + 0.001 * v, 0.999 * hi + 0.001 * v])
+    assert np.array_equal(plain.fl16(inner).view(np.uint16), np.concatenate([h, h]))
+
+
+def test_f16_decision_rule():
+    """The binary32 side's binary16 value passes when the binary64 value lies within the error
+    bound of the reals rounding to it: a neighbour across a nearby boundary, or a value several
+    steps away when the bound spans them; otherwise the check raises."""
+    ulp = 2.0**-24  # binary16 step in [2^-14, 2^-13)
+    x = 6.88991663864158e-05
+    h_plain = plain.fl16(np.array([x])).view(np.uint16)
+    far = (h_plain - 5).astype(np.uint16)  # five steps below
+    st = PP.PlainStats()
+    PP._check_f16("h", np.array([x]), h_plain, np.array([1e-12]), st, "same")
+    assert st.forced["h"] == 0
+    PP._check_f16("h", np.array([x]), far, np.array([1.6e-5]), st, "wide bound")
+    assert st.forced["h"] == 1
+    with pytest.raises(PP.PlainMismatch):
+        PP._check_f16("h", np.array([x]), far, np.array([3 * ulp]), st, "narrow bound")
+    # a neighbour: x just above the midpoint with the next value down
+    v = float(np.float16(1.0))
+    xb = 1 - 2.0**-12 + 1e-9
+    PP._check_f16("r", np.array([xb]), _h(1.0 - 2.0**-11)[None], np.array([2e-9]), st, "nb")
+    with pytest.raises(PP.PlainMismatch):
+        PP._check_f16("r", np.array([xb]), _h(1.0 - 2.0**-11)[None], np.array([5e-10]), st, "nb2")
+    assert v == 1.0
+
+
+def test_random_plan_2398_pivot_entry_left_small_by_cancellation(orc):
+    """A GDN pivot head (decay-first gate order, contrast geometry) whose step-0 state holds an
+    entry near 6.9e-5 left by cancellation: the binary32 bound of that entry spans several
+    binary16 steps, and the specification's value is five steps from the binary64 rounding."""
+    import test_gpu_random_plans as R
+    w, bits, piv, om, mode = R._random_case(2398)
+    assert (w.kind, w.d, w.order) == ("gdn", 128, 1)
+    st = _spec_vs_plain(w, [3], 1, plan=P.oracle_plan(w))
+    assert st.forced["h"] >= 1 and st.worst_ratio <= 1.0
