@@ -457,19 +457,39 @@ __device__ __forceinline__ float col_factor1(float num, float sq, float c0, uint
 // G*lane + g, every wave then reads 1/c_hat of its G columns, and wave 0 stores the lane's G
 // binary16 factors with one store (cblk may be null), so each segment's factor block is written
 // by whole words.
-template <int D, typename SM>
-__device__ __forceinline__ void col_refit(SM& sm, float* csh, int w, int lane, float c0w,
-                                          uint16_t* cblk, float* ic, unsigned& fl) {
+//
+//
+// kTest: waves w < G also pass their column's maximum ymax (the largest |y| of column
+// G*lane + w over every row) and the head's qmax, and every wave gets back whether no code of
+// the tile reaches the clamp: every column's fma(ymax, 1/c_hat, kMagic) lies at most qmax above
+// kMagic, and its least-squares sums are not NaN.  The rounding of fma(y, ic, kMagic) is
+// monotone in y and symmetric about kMagic (an even integer, unit spacing around it), so then
+// every |y| <= ymax of the column rounds inside +-qmax and the clamp is the identity for the
+// whole tile.  An infinite maximum fails the test; a NaN entry (which the maximum skips) makes
+// the column's sum of squares NaN and fails it there.
+template <int D, bool kTest = false, typename SM>
+__device__ __forceinline__ bool col_refit(SM& sm, float* csh, int w, int lane, float c0w,
+                                          uint16_t* cblk, float* ic, unsigned& fl,
+                                          float ymax = 0.0f, float qm = 0.0f) {
   constexpr int G = Geo<D>::G;
   uint16_t* const chs = reinterpret_cast<uint16_t*>(csh + 2 * D);
+  int* const clamp_free = reinterpret_cast<int*>(csh + 2 * D + D / 2);  // [G] wave verdicts
   if (w < G) {
     const float n = xwave_sum_col<D>(sm, 0, lane, w), q = xwave_sum_col<D>(sm, 1, lane, w);
     uint16_t ch;
-    csh[D + G * lane + w] = col_factor1(n, q, c0w, ch, fl);
+    const float icw = col_factor1(n, q, c0w, ch, fl);
+    csh[D + G * lane + w] = icw;
     chs[G * lane + w] = ch;
+    if constexpr (kTest) {
+      const bool inside = __builtin_fmaf(ymax, icw, kMagic) <= kMagic + qm && q == q;
+      const bool all = __builtin_amdgcn_ballot_w64(inside) == ~0ull;
+      if (lane == 0) clamp_free[w] = all;
+    }
   }
   __syncthreads();
   sfor<G>([&](auto gg) { ic[CI(gg)] = csh[D + G * lane + CI(gg)]; });
+  bool free_all = kTest;
+  if constexpr (kTest) sfor<G>([&](auto gg) { free_all = free_all && clamp_free[CI(gg)] != 0; });
   if (w == 0 && cblk) {
     if constexpr (G == 2) {
       reinterpret_cast<uint32_t*>(cblk)[lane] = reinterpret_cast<const uint32_t*>(chs)[lane];
@@ -477,6 +497,7 @@ __device__ __forceinline__ void col_refit(SM& sm, float* csh, int w, int lane, f
       cblk[lane] = chs[lane];
     }
   }
+  return free_all;
 }
 
 // |S| partial sums of each row over this lane's columns, transposed through LDS.
@@ -828,9 +849,10 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
     xwave_max_put<D>(sm, w, lane, mx);
     __syncthreads();
     float* const csh = col_share<D>(sm);
-    float c0w = 0.0f;  // c0 of column G*lane + w (waves w < G)
+    float c0w = 0.0f, ymaxw = 0.0f;  // c0 and max |y| of column G*lane + w (waves w < G)
     if (w < G) {
-      c0w = xwave_max_col<D>(sm, lane, w) * IQ;
+      ymaxw = xwave_max_col<D>(sm, lane, w);
+      c0w = ymaxw * IQ;
       csh[G * lane + w] = rcp0(c0w);
     }
     if constexpr (kRead) {
@@ -852,17 +874,27 @@ __device__ __forceinline__ void gdn_tile(const StepArgs& A, int b, long long slo
     xwave_put<D>(sm, 0, w, lane, num);  // slot 0 (u) and slot 1 (readout) were last read
     xwave_put<D>(sm, 1, w, lane, sq);   // before the barriers above
     __syncthreads();
-    col_refit<D>(sm, csh, w, lane, c0w, cblk, ic, fl);
+    const bool clamp_free = col_refit<D, true>(sm, csh, w, lane, c0w, cblk, ic, fl, ymaxw, QM);
 
-    // ---- phase 5: final requantization and packing
+    // ---- phase 5: final requantization and packing.  When no code of the tile can reach
+    // +-qmax (the usual case after the refit) the clamp is the identity and is left out: the
+    // same bits, one instruction per entry fewer.
     uint32_t acc = 0;
     auto store = [&](auto wi, uint32_t x) {
       __builtin_nontemporal_store(x, &wl[CI(wi) * 64]);
     };
-    sfor<R * G>([&](auto kk) {
-      constexpr int K = CI(kk), r = K / G, g = K % G;
-      put_code<BITS, K>(acc, __builtin_bit_cast(uint32_t, quant_off(S[r][g], ic[g], QM)), store);
-    });
+    if (clamp_free) {
+      sfor<R * G>([&](auto kk) {
+        constexpr int K = CI(kk), r = K / G, g = K % G;
+        put_code<BITS, K>(acc, __builtin_bit_cast(uint32_t, fma_magic(S[r][g], ic[g])), store);
+      });
+    } else {
+      sfor<R * G>([&](auto kk) {
+        constexpr int K = CI(kk), r = K / G, g = K % G;
+        put_code<BITS, K>(acc, __builtin_bit_cast(uint32_t, quant_off(S[r][g], ic[g], QM)),
+                          store);
+      });
+    }
   }
   raise_flags(A, fl);
 }
